@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the GQA block forward (Llama 3.1 8B attention block) on one MI355X.
+
+Headline: prefill B=1, T=2048, causal, the whole block (fused QKV projection
+with rotation, grouped flash attention, output projection) per step, in
+TFLOP/s of algorithmic work (only unmasked query/key pairs count). Also
+measured in the same run: decode (B=64, one token at position 8191 over a
+bf16 KV cache of 8192 rows) in HBM GB/s, and prefill at B=8, T=4096 and at
+B=1, T=131072.
+
+Prints one JSON line. Inputs are seeded synthetic bf16 values resident in HBM
+before the timed region. `roofline` describes the kernel that takes the most
+time in the headline step, timed with HIP events on the stream it runs on;
+`cpu_baseline` is the fp64 CPU oracle timed on this host on the full headline
+workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PARAMS_PER_BLOCK = 41_943_040  # W_Q + W_K + W_V + W_O
+
+
+def prefill_flops(B, T, start_pos=0):
+    """Algorithmic flops: the four projections plus 4*32*128 per unmasked (q, k) pair."""
+    pairs = T * start_pos + T * (T + 1) // 2
+    return 2 * B * T * PARAMS_PER_BLOCK + 4 * B * 32 * 128 * pairs
+
+
+def stage_flops(B, T):
+    M = B * T
+    return {"qkv_rope": 2 * M * 4096 * 6144,
+            "attention": 4 * B * 32 * 128 * (T * (T + 1) // 2),
+            "out_proj": 2 * M * 4096 * 4096}
+
+
+def decode_bytes(B, kv_len):
+    """Algorithmic HBM bytes of one decode step: weights, cached K/V rows read,
+    new K/V row written, x, fp32 Δ, one rotation row."""
+    return (2 * PARAMS_PER_BLOCK + B * (kv_len - 1) * 1024 * 2 * 2 + B * 1024 * 2 * 2
+            + B * 4096 * 2 + B * 4096 * 4 + 64 * 2 * 4)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import gqa_inputs as gi
+    import grouped_query_attention_amd as gqa
+
+    dev = torch.device("cuda:0")
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def time_steps(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return e0.elapsed_time(e1) / steps, wall
+
+    # ---------------- headline: prefill B=1 T=2048 ----------------
+    B, T = 1, 2048
+    log(f"[bench] prefill B={B} T={T}: generating inputs")
+    inp = gi.make_block_inputs(2, B, T)
+    x = up(inp.x)
+    w = [up(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo)]
+    rope = torch.from_numpy(gqa.rope_table(np.arange(T))).to(dev)
+    out = torch.empty((B, T, 4096), dtype=torch.float32, device=dev)
+    ws = torch.empty(gqa.prefill_workspace_bytes(B, T), dtype=torch.uint8, device=dev)
+    step = lambda: gqa.block_forward(x, *w, rope, causal=True, out=out, workspace=ws)
+    ms, wall_ms = time_steps(step, args.steps, args.warmup)
+    F = prefill_flops(B, T)
+    value = F / (ms * 1e-3) / 1e12
+    log(f"[bench] prefill C2: {ms:.4f} ms/step (wall {wall_ms:.4f}), {value:.1f} TFLOP/s")
+
+    # per-kernel timing (stage entries launch exactly the kernels of the step)
+    q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
+    hbuf = gqa.attention(q_r, k_r, v, causal=True)
+    stages = {
+        "qkv_rope": ("gemm_nt_kernel<128,128,QKV_ROPE>",
+                     lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
+        "attention": ("flash_fwd_kernel", lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf)),
+        "out_proj": ("gemm_nt_kernel<128,128,OUT_F32>",
+                     lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
+    }
+    sf = stage_flops(B, T)
+    kern = {}
+    for name, (kname, fn) in stages.items():
+        kms, _ = time_steps(fn, args.steps, args.warmup)
+        kern[name] = {"kernel": kname, "ms": kms, "tflops": sf[name] / (kms * 1e-3) / 1e12}
+        kern[name]["frac"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
+        log(f"[bench]   {name}: {kms:.4f} ms, {kern[name]['tflops']:.1f} TFLOP/s")
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    roofline = {"bound": "mfma", "kernel": kern[dom]["kernel"], "stage": dom,
+                "achieved": round(kern[dom]["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(kern[dom]["frac"], 4), "traffic": None,
+                "flops_per_launch": sf[dom], "avg_launch_ms": round(kern[dom]["ms"], 5)}
+
+    result = {
+        "metric": "GQA block fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Llama-3.1-8B GQA attention block forward, prefill, causal",
+                   "B": B, "T": T, "d": 4096, "q_heads": 32, "kv_heads": 8, "d_head": 128,
+                   "rope_theta": 500000.0, "flops_per_step": F,
+                   "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                        for kk, vv in d.items()} for k, d in kern.items()},
+    }
+    del q_r, k_r, v, hbuf
+
+    # ---------------- other configurations ----------------
+    extra = {}
+    if not args.quick:
+        # decode B=64, start_pos 8191, cache 8192 rows
+        Bd, S, sp = 64, 8192, 8191
+        log("[bench] decode B=64 kv=8192: generating cache")
+        dinp = gi.make_block_inputs(4, Bd, 1, cache_len=S)
+        dx = up(dinp.x[:, 0])
+        dw = [up(a) for a in (dinp.wq, dinp.wk, dinp.wv, dinp.wo)]
+        kc, vc = up(dinp.k_cache), up(dinp.v_cache)
+        del dinp
+        drope = torch.from_numpy(gqa.rope_table([sp])[0]).to(dev)
+        dout = torch.empty((Bd, 4096), dtype=torch.float32, device=dev)
+        dws = torch.empty(gqa.decode_workspace_bytes(Bd, S), dtype=torch.uint8, device=dev)
+        dstep = lambda: gqa.decode_forward(dx, *dw, drope, kc, vc, sp, out=dout, workspace=dws)
+        dms, _ = time_steps(dstep, args.steps, args.warmup)
+        nbytes = decode_bytes(Bd, S)
+        qd = torch.zeros((Bd, 32, 128), dtype=torch.bfloat16, device=dev)
+        hd = torch.empty_like(qd)
+        ams, _ = time_steps(lambda: gqa.decode_attention(qd, kc, vc, S, h_out=hd, workspace=dws),
+                            args.steps, args.warmup)
+        kv_bytes = Bd * S * 1024 * 2 * 2
+        extra["decode_B64_kv8192"] = {
+            "ms": round(dms, 5), "GB/s": round(nbytes / (dms * 1e-3) / 1e9, 1),
+            "frac_of_hbm": round(nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes_per_step": nbytes,
+            "attention_kernel": {"kernel": "decode_splitkv_kernel+decode_merge_kernel",
+                                 "ms": round(ams, 5),
+                                 "GB/s": round(kv_bytes / (ams * 1e-3) / 1e9, 1),
+                                 "frac_of_hbm": round(kv_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
+        log(f"[bench] decode: {dms:.4f} ms, {extra['decode_B64_kv8192']['GB/s']} GB/s")
+        del kc, vc, dws
+
+        for (Bp, Tp, seed, steps) in ((8, 4096, 3, max(3, args.steps // 4)),
+                                      (1, 131072, 5, 2)):
+            log(f"[bench] prefill B={Bp} T={Tp}: generating inputs")
+            pinp = gi.make_block_inputs(seed, Bp, Tp)
+            px = up(pinp.x)
+            pw = [up(a) for a in (pinp.wq, pinp.wk, pinp.wv, pinp.wo)]
+            del pinp
+            prope = torch.from_numpy(gqa.rope_table(np.arange(Tp))).to(dev)
+            pout = torch.empty((Bp, Tp, 4096), dtype=torch.float32, device=dev)
+            pws = torch.empty(gqa.prefill_workspace_bytes(Bp, Tp), dtype=torch.uint8, device=dev)
+            pstep = lambda: gqa.block_forward(px, *pw, prope, causal=True, out=pout, workspace=pws)
+            pms, _ = time_steps(pstep, steps, 1)
+            Fp = prefill_flops(Bp, Tp)
+            tf = Fp / (pms * 1e-3) / 1e12
+            extra[f"prefill_B{Bp}_T{Tp}"] = {"ms": round(pms, 4), "TFLOP/s": round(tf, 1),
+                                             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                             "flops_per_step": Fp, "steps": steps}
+            log(f"[bench] prefill B={Bp} T={Tp}: {pms:.3f} ms, {tf:.1f} TFLOP/s")
+            del px, pw, pout, pws
+            torch.cuda.empty_cache()
+    result["other_configs"] = extra
+
+    # ---------------- CPU oracle baseline (full headline workload) ----------------
+    if not args.no_cpu:
+        import threadpoolctl
+        from oracle import gqa_oracle as O
+        cores = len(os.sched_getaffinity(0))
+        with threadpoolctl.threadpool_limits(cores):
+            used = max([d["num_threads"] for d in threadpoolctl.threadpool_info()] or [1])
+            log(f"[bench] cpu oracle on {used} threads: B=1 T=2048 full forward")
+            t0 = time.perf_counter()
+            ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)
+            cpu_s = time.perf_counter() - t0
+        step()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.float64)
+        d = ref["delta"]
+        result["cpu_baseline"] = {"value": round(F / cpu_s / 1e12, 5), "unit": "TFLOP/s",
+                                  "cores": used, "kind": "oracle",
+                                  "sample": "full prefill B=1 T=2048 causal, one forward, fp64 numpy",
+                                  "seconds": round(cpu_s, 3)}
+        result["parity_vs_oracle"] = {
+            "relL2": float(np.linalg.norm(got - d) / np.linalg.norm(d)),
+            "maxabs": float(np.max(np.abs(got - d)))}
+        log(f"[bench] cpu oracle {cpu_s:.2f} s; parity {result['parity_vs_oracle']}")
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,250 @@
+"""Python binding of libgqa, the MI355X (gfx950) grouped-query-attention block library.
+
+Argument marshalling only: every step of the block runs in the library's HIP
+kernels. torch supplies device memory and the current stream; tensors are
+passed to the C ABI as raw pointers. There is no fallback: if libgqa.so is
+missing or cannot be loaded, every call raises.
+
+Names follow include/gqa.h:
+    block_forward, decode_forward, qkv_rope, attention, output_projection,
+    decode_attention, rope_table, prefill_workspace_bytes,
+    decode_workspace_bytes, dims.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgqa.so")
+
+D_MODEL, N_HEADS, N_KV_HEADS, D_HEAD, N_PAIRS = 4096, 32, 8, 128, 64
+ROPE_THETA = 500000.0
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    """A libgqa entry point returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int):
+        msg = _load().gqa_status_string(status).decode()
+        super().__init__(f"{fn}: {msg} (status {status})")
+        self.status = status
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libgqa.so not built at {LIB_PATH}; run "
+                           "`python -m grouped_query_attention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    sig = {
+        "gqa_status_string": (ctypes.c_char_p, [I]),
+        "gqa_dims": (None, [P, P, P, P]),
+        "gqa_rope_table": (I, [P, I, D, P]),
+        "gqa_prefill_workspace_bytes": (Z, [I, I]),
+        "gqa_decode_workspace_bytes": (Z, [I, I]),
+        "gqa_block_forward": (I, [P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
+        "gqa_decode_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P, Z, P]),
+        "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, P]),
+        "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P]),
+        "gqa_output_projection": (I, [P, P, I, P, P]),
+        "gqa_decode_attention": (I, [P, P, P, I, I, I, P, P, Z, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def lib():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def exported_symbols():
+    return ["gqa_status_string", "gqa_dims", "gqa_rope_table", "gqa_prefill_workspace_bytes",
+            "gqa_decode_workspace_bytes", "gqa_block_forward", "gqa_decode_forward",
+            "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention"]
+
+
+# --- helpers -------------------------------------------------------------------------
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise GQAError(fn, st)
+
+
+def _req(t, dtype, shape, name):
+    import torch
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+# --- host-side entries ----------------------------------------------------------------
+
+def dims():
+    a, b, c, d = (ctypes.c_int() for _ in range(4))
+    _load().gqa_dims(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(d))
+    return a.value, b.value, c.value, d.value
+
+
+def rope_table(positions, theta: float = ROPE_THETA) -> np.ndarray:
+    """(cos, sin) table [n, 64, 2] float32 for the given positions (host computation)."""
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    out = np.empty((pos.size, N_PAIRS, 2), dtype=np.float32)
+    _check("gqa_rope_table", _load().gqa_rope_table(
+        pos.ctypes.data if pos.size else None, int(pos.size), float(theta),
+        out.ctypes.data if pos.size else None))
+    return out
+
+
+def prefill_workspace_bytes(B: int, T: int) -> int:
+    return int(_load().gqa_prefill_workspace_bytes(B, T))
+
+
+def decode_workspace_bytes(B: int, S_max: int) -> int:
+    return int(_load().gqa_decode_workspace_bytes(B, S_max))
+
+
+# --- device entries -------------------------------------------------------------------
+
+def block_forward(x, w_q, w_k, w_v, w_o, rope, *, causal: bool = True, mask=None,
+                  out=None, h_out=None, workspace=None, stream=None):
+    """Δ = GQA block forward for x [B, T, 4096] bf16; returns out [B, T, 4096] fp32."""
+    import torch
+    B, T, _ = x.shape
+    _req(x, torch.bfloat16, (B, T, D_MODEL), "x")
+    _req(rope, torch.float32, (T, N_PAIRS, 2), "rope")
+    if mask is not None:
+        _req(mask, torch.float32, (T, T), "mask")
+    if out is None:
+        out = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=x.device)
+    _req(out, torch.float32, (B, T, D_MODEL), "out")
+    if h_out is not None:
+        _req(h_out, torch.bfloat16, (B, T, N_HEADS, D_HEAD), "h_out")
+    need = prefill_workspace_bytes(B, T)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = _load().gqa_block_forward(
+        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(mask),
+        int(bool(causal)), B, T, T, _ptr(out), _ptr(h_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gqa_block_forward", st)
+    return out
+
+
+def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,
+                   out=None, h_out=None, workspace=None, stream=None):
+    """One new position per sequence at start_pos; x [B, 4096]; returns out [B, 4096] fp32.
+
+    Writes the new rotated key and value into cache slot start_pos.
+    """
+    import torch
+    B = x.shape[0]
+    S_max = k_cache.shape[1]
+    _req(x, torch.bfloat16, (B, D_MODEL), "x")
+    _req(rope, torch.float32, (N_PAIRS, 2), "rope")
+    _req(k_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "k_cache")
+    _req(v_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "v_cache")
+    if out is None:
+        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B, S_max), dtype=torch.uint8,
+                                device=x.device)
+    st = _load().gqa_decode_forward(
+        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
+        _ptr(v_cache), B, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gqa_decode_forward", st)
+    return out
+
+
+def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None):
+    """Q_r [B,T,32,128], K_r [B,T,8,128], V [B,T,8,128] (bf16) for x [B,T,4096]."""
+    import torch
+    B, T, _ = x.shape
+    _req(x, torch.bfloat16, (B, T, D_MODEL), "x")
+    dev = x.device
+    if q_r is None:
+        q_r = torch.empty((B, T, N_HEADS, D_HEAD), dtype=torch.bfloat16, device=dev)
+    if k_r is None:
+        k_r = torch.empty((B, T, N_KV_HEADS, D_HEAD), dtype=torch.bfloat16, device=dev)
+    if v is None:
+        v = torch.empty((B, T, N_KV_HEADS, D_HEAD), dtype=torch.bfloat16, device=dev)
+    st = _load().gqa_qkv_rope(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(rope), B, T,
+                              _ptr(q_r), _ptr(k_r), _ptr(v), _stream(stream))
+    _check("gqa_qkv_rope", st)
+    return q_r, k_r, v
+
+
+def attention(q_r, k_r, v, *, causal: bool = True, mask=None, h_out=None, stream=None):
+    """H [B,T,32,128] bf16 from rotated queries/keys and values."""
+    import torch
+    B, T = q_r.shape[:2]
+    kv_len = k_r.shape[1]
+    if h_out is None:
+        h_out = torch.empty((B, T, N_HEADS, D_HEAD), dtype=torch.bfloat16, device=q_r.device)
+    st = _load().gqa_attention(_ptr(q_r), _ptr(k_r), _ptr(v), _ptr(mask), int(bool(causal)),
+                               B, T, kv_len, _ptr(h_out), _stream(stream))
+    _check("gqa_attention", st)
+    return h_out
+
+
+def output_projection(h, w_o, *, out=None, stream=None):
+    """out [M,4096] fp32 = h [M,4096] bf16 · w_oᵀ (h may be [B,T,32,128])."""
+    import torch
+    M = h.numel() // D_MODEL
+    if out is None:
+        out = torch.empty((M, D_MODEL), dtype=torch.float32, device=h.device)
+    st = _load().gqa_output_projection(_ptr(h), _ptr(w_o), M, _ptr(out), _stream(stream))
+    _check("gqa_output_projection", st)
+    return out
+
+
+def decode_attention(q_r, k_cache, v_cache, kv_len: int, *, h_out=None, workspace=None,
+                     stream=None):
+    """H [B,32,128] bf16 for queries q_r [B,32,128] over cache keys 0..kv_len-1."""
+    import torch
+    B, S_max = k_cache.shape[:2]
+    if h_out is None:
+        h_out = torch.empty((B, N_HEADS, D_HEAD), dtype=torch.bfloat16, device=q_r.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B, S_max), dtype=torch.uint8,
+                                device=q_r.device)
+    st = _load().gqa_decode_attention(_ptr(q_r), _ptr(k_cache), _ptr(v_cache), B, S_max,
+                                      int(kv_len), _ptr(h_out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(stream))
+    _check("gqa_decode_attention", st)
+    return h_out

@@ -1,0 +1,243 @@
+// C ABI of libgqa: argument validation (host only, before any HIP call),
+// workspace carve-up, and the kernel sequence of each entry point.
+// Semantics, layouts and error codes are documented in include/gqa.h.
+
+#include <cmath>
+#include <cstdint>
+
+#include "gqa.h"
+#include "gqa_device.h"
+#include "gqa_launch.h"
+
+namespace {
+
+using gqa::D_HEAD;
+using gqa::D_MODEL;
+using gqa::N_HEADS;
+using gqa::N_KV;
+
+constexpr size_t KV_W = (size_t)N_KV * D_HEAD;  // 1024 features of K or V per token
+
+inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+struct PrefillWs {
+  size_t q, k, v, h, total;
+};
+
+inline PrefillWs prefill_layout(long long M) {
+  PrefillWs w{};
+  const size_t m = (size_t)M;
+  w.q = 0;
+  w.k = w.q + align_up(m * D_MODEL * 2);
+  w.v = w.k + align_up(m * KV_W * 2);
+  w.h = w.v + align_up(m * KV_W * 2);
+  w.total = w.h + align_up(m * D_MODEL * 2);
+  return w;
+}
+
+struct DecodeWs {
+  size_t q, h, part, total;
+};
+
+inline DecodeWs decode_layout(int B, int S_max) {
+  DecodeWs w{};
+  w.q = 0;
+  w.h = align_up((size_t)B * D_MODEL * 2);
+  w.part = w.h + align_up((size_t)B * D_MODEL * 2);
+  w.total = w.part + align_up(gqa::decode_partials_bytes(B, S_max));
+  return w;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
+
+inline bool tokens_ok(int B, int T) {
+  return B >= 1 && T >= 1 && (long long)B * T <= GQA_MAX_TOKENS;
+}
+
+int check_weights(const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
+                  const gqa_bf16* wo) {
+  if (!wq || !wk || !wv || !wo) return GQA_ERR_NULL;
+  if (misaligned(wq) || misaligned(wk) || misaligned(wv) || misaligned(wo)) return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gqa_status_string(int s) {
+  switch (s) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_NULL: return "GQA_ERR_NULL: a required pointer is NULL";
+    case GQA_ERR_SHAPE: return "GQA_ERR_SHAPE: a size argument is out of range";
+    case GQA_ERR_ALIGN: return "GQA_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case GQA_ERR_WORKSPACE: return "GQA_ERR_WORKSPACE: workspace missing or too small";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: request not implemented";
+    case GQA_ERR_HIP: return "GQA_ERR_HIP: a HIP launch failed";
+    case GQA_ERR_ARG: return "GQA_ERR_ARG: inconsistent arguments";
+    default: return "GQA_ERR_UNKNOWN";
+  }
+}
+
+void gqa_dims(int* d_model, int* n_heads, int* n_kv_heads, int* d_head) {
+  if (d_model) *d_model = GQA_D_MODEL;
+  if (n_heads) *n_heads = GQA_N_HEADS;
+  if (n_kv_heads) *n_kv_heads = GQA_N_KV_HEADS;
+  if (d_head) *d_head = GQA_D_HEAD;
+}
+
+int gqa_rope_table(const int32_t* positions, int n, double theta, float* table) {
+  if (n < 0 || !(theta > 1.0)) return GQA_ERR_SHAPE;
+  if (n == 0) return GQA_OK;
+  if (!positions || !table) return GQA_ERR_NULL;
+  double omega[GQA_N_PAIRS];
+  for (int j = 0; j < GQA_N_PAIRS; ++j)
+    omega[j] = std::exp(-(2.0 * j / (double)GQA_D_HEAD) * std::log(theta));
+  for (int i = 0; i < n; ++i) {
+    const double t = (double)positions[i];
+    for (int j = 0; j < GQA_N_PAIRS; ++j) {
+      const double ang = t * omega[j];
+      table[(size_t)i * 2 * GQA_N_PAIRS + 2 * j] = (float)std::cos(ang);
+      table[(size_t)i * 2 * GQA_N_PAIRS + 2 * j + 1] = (float)std::sin(ang);
+    }
+  }
+  return GQA_OK;
+}
+
+size_t gqa_prefill_workspace_bytes(int B, int T) {
+  if (!tokens_ok(B, T)) return 0;
+  return prefill_layout((long long)B * T).total;
+}
+
+size_t gqa_decode_workspace_bytes(int B, int S_max) {
+  if (B < 1 || S_max < 1) return 0;
+  return decode_layout(B, S_max).total;
+}
+
+int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                 const gqa_bf16* w_v, const float* rope, int B, int T, gqa_bf16* q_r,
+                 gqa_bf16* k_r, gqa_bf16* v, void* stream) {
+  if (!x || !rope || !q_r || !k_r || !v || !w_q || !w_k || !w_v) return GQA_ERR_NULL;
+  if (!tokens_ok(B, T)) return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(rope) || misaligned(q_r) || misaligned(k_r) ||
+      misaligned(v) || misaligned(w_q) || misaligned(w_k) || misaligned(w_v))
+    return GQA_ERR_ALIGN;
+  const long long M = (long long)B * T;
+  return hip_status(gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q_r,
+                                         (long long)T * D_MODEL, D_MODEL, k_r, v,
+                                         (long long)T * KV_W, KV_W, (hipStream_t)stream));
+}
+
+int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
+                  const float* mask, int causal, int B, int T, int kv_len, gqa_bf16* h_out,
+                  void* stream) {
+  if (!q_r || !k_r || !v || !h_out) return GQA_ERR_NULL;
+  if (causal != 0 && causal != 1) return GQA_ERR_ARG;
+  if (causal && mask) return GQA_ERR_ARG;
+  if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
+  if (kv_len != T) return GQA_ERR_UNSUPPORTED;
+  if (misaligned(q_r) || misaligned(k_r) || misaligned(v) || misaligned(h_out) ||
+      (mask && misaligned(mask)))
+    return GQA_ERR_ALIGN;
+  return hip_status(gqa::launch_flash_attention(q_r, k_r, v, (long long)kv_len * KV_W, mask,
+                                                causal, B, T, kv_len, 0, h_out,
+                                                (hipStream_t)stream));
+}
+
+int gqa_output_projection(const gqa_bf16* h, const gqa_bf16* w_o, int M, float* out,
+                          void* stream) {
+  if (!h || !w_o || !out) return GQA_ERR_NULL;
+  if (M < 1 || M > GQA_MAX_TOKENS) return GQA_ERR_SHAPE;
+  if (misaligned(h) || misaligned(w_o) || misaligned(out)) return GQA_ERR_ALIGN;
+  return hip_status(gqa::launch_out_proj(h, w_o, M, out, (hipStream_t)stream));
+}
+
+int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                      const float* mask, int causal, int B, int T, int kv_len, float* out,
+                      gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!x || !rope || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st != GQA_OK) return st;
+  if (causal != 0 && causal != 1) return GQA_ERR_ARG;
+  if (causal && mask) return GQA_ERR_ARG;
+  if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
+  if (kv_len != T) return GQA_ERR_UNSUPPORTED;
+  if (misaligned(x) || misaligned(rope) || misaligned(out) || (mask && misaligned(mask)) ||
+      (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const long long M = (long long)B * T;
+  const PrefillWs L = prefill_layout(M);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  auto* k = reinterpret_cast<gqa_bf16*>(ws + L.k);
+  auto* v = reinterpret_cast<gqa_bf16*>(ws + L.v);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
+                                      (long long)T * D_MODEL, D_MODEL, k, v,
+                                      (long long)T * KV_W, KV_W, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
+                                  h, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, s));
+}
+
+int gqa_decode_attention(const gqa_bf16* q_r, const gqa_bf16* k_cache,
+                         const gqa_bf16* v_cache, int B, int S_max, int kv_len,
+                         gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!q_r || !k_cache || !v_cache || !h_out) return GQA_ERR_NULL;
+  if (B < 1 || B > GQA_MAX_TOKENS || S_max < 1 || kv_len < 1 || kv_len > S_max)
+    return GQA_ERR_SHAPE;
+  if (misaligned(q_r) || misaligned(k_cache) || misaligned(v_cache) || misaligned(h_out))
+    return GQA_ERR_ALIGN;
+  const DecodeWs L = decode_layout(B, S_max);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.part);
+  return hip_status(gqa::launch_decode_attention(q_r, k_cache, v_cache, B, S_max, kv_len, part,
+                                                 h_out, (hipStream_t)stream));
+}
+
+int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                       const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                       gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max, int start_pos,
+                       float* out, gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st != GQA_OK) return st;
+  if (B < 1 || B > GQA_MAX_TOKENS || S_max < 1 || start_pos < 0 || start_pos >= S_max)
+    return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
+      misaligned(out) || (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const DecodeWs L = decode_layout(B, S_max);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipStream_t s = (hipStream_t)stream;
+  const long long cache_bstride = (long long)S_max * KV_W;
+
+  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, B, 1, q, D_MODEL, 0,
+                                      k_cache + (size_t)start_pos * KV_W,
+                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, 0, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, B, out, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Device-side helpers shared by the libgqa kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int D_MODEL = 4096;
+constexpr int N_HEADS = 32;
+constexpr int N_KV = 8;
+constexpr int D_HEAD = 128;
+constexpr int N_REP = N_HEADS / N_KV;     // query heads per KV head (4)
+constexpr int N_QKV = D_MODEL + 2 * N_KV * D_HEAD;  // 6144 fused projection columns
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Operand lane layout: lane l holds row/column (l & 31), k = 8*(l >> 5) .. +7.
+// Result lane layout: lane l holds column (l & 31), rows 8*(i/4) + 4*(l>>5) + (i&3).
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).
+// Operand lane layout: lane l holds row/column (l & 15), k = 8*(l >> 4) .. +7.
+// Result lane layout: lane l holds column (l & 15), rows 4*(l>>4) + i.
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace gqa

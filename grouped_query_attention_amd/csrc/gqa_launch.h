@@ -1,0 +1,39 @@
+// Internal launchers of libgqa (host side). Arguments are validated by the
+// C ABI layer before any of these is called; these only enqueue kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Fused Q/K/V projection + pair rotation over M tokens (T tokens per sequence;
+// rope row = token % T). Destination of token m = b*T + t:
+//   Q row: q_dst + b*q_bstride + t*q_rstride           (4096 elements)
+//   K/V row: k_dst/v_dst + b*kv_bstride + t*kv_rstride  (1024 elements)
+hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
+                           const uint16_t* wv, const float* rope, int M, int T,
+                           uint16_t* q_dst, long long q_bstride, long long q_rstride,
+                           uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
+                           long long kv_rstride, hipStream_t s);
+
+// out[M][4096] (fp32) = h[M][4096] · w_oᵀ
+hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
+                           hipStream_t s);
+
+// Prefill grouped flash attention. q_r/h_out [B][T][32][128]; k/v rows of
+// sequence b start at k + b*kv_bstride (row stride 1024 elements); query i is
+// at position q_pos0 + i; keys 0..kv_len-1.
+hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
+                                  long long kv_bstride, const float* mask, int causal, int B,
+                                  int T, int kv_len, int q_pos0, uint16_t* h_out,
+                                  hipStream_t s);
+
+// Split-KV decode attention: q_r [B][32][128]; caches [B][S_max][8][128];
+// keys 0..kv_len-1; h_out [B][32][128]. `partials` needs decode_partials_bytes.
+size_t decode_partials_bytes(int B, int S_max);
+hipError_t launch_decode_attention(const uint16_t* q_r, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, int B, int S_max, int kv_len,
+                                   float* partials, uint16_t* h_out, hipStream_t s);
+
+}  // namespace gqa
