@@ -282,12 +282,17 @@ def block_forward_rows(x, wq, wk, wv, wo, n_heads: int, n_kv: int, rows,
     n_rep = n_heads // n_kv
     inv_sqrt = 1.0 / math.sqrt(dh)
     h = np.empty((len(rows), n_heads, dh))
-    for ri, t in enumerate(rows):
-        for hd in range(n_heads):
-            g = hd // n_rep
-            s = (k_r[: t + 1, g, :] @ q_r[ri, hd]) * inv_sqrt   # keys 0..t unmasked
-            a = softmax_rows(s[None, :])[0]
-            h[ri, hd] = a @ v[: t + 1, g, :]
+    keys = np.arange(last)
+    for g in range(n_kv):
+        kg = np.ascontiguousarray(k_r[:, g, :])        # [last, dh]
+        vg = np.ascontiguousarray(v[:, g, :])
+        for r0 in range(0, len(rows), 64):
+            r1 = min(len(rows), r0 + 64)
+            # additive causal mask of the sampled rows: -inf where key j > position t
+            m = np.where(keys[None, :] > rows[r0:r1, None], -np.inf, 0.0)
+            for hd in range(g * n_rep, (g + 1) * n_rep):
+                s = (q_r[r0:r1, hd, :] @ kg.T) * inv_sqrt + m
+                h[r0:r1, hd] = softmax_rows(s) @ vg
     hm = h.reshape(len(rows), n_heads * dh)
     return dict(rows=rows, h=hm, delta=project(hm, wo))
 
