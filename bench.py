@@ -123,10 +123,10 @@ def main():
     q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
     hbuf = gqa.attention(q_r, k_r, v, causal=True)
     stages = {
-        "qkv_rope": ("gemm_nt_kernel<128,128,QKV_ROPE>",
+        "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
                      lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
         "attention": ("flash_fwd_kernel", lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf)),
-        "out_proj": ("gemm_nt_kernel<128,128,OUT_F32>",
+        "out_proj": ("gemm_nt_kernel (W_O GEMM, fp32 epilogue)",
                      lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
     }
     sf = stage_flops(B, T)

@@ -8,9 +8,14 @@
 //  * out_proj: Δ = H · W_Oᵀ in fp32 (the last equation; Merge and project page).
 //
 // Both are "NT" products: each operand is contiguous along the 4096-long
-// reduction axis. A workgroup of 4 waves computes a TOKxFEAT tile with a
-// K step of 64; tiles of both operands are staged in LDS (double buffered,
-// XOR-swizzled 16-byte chunks so fragment reads are bank-conflict free).
+// reduction axis. A workgroup computes a TOK x FEAT tile with a K step of 64.
+// Operand tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
+// register staging) through a ring of STAGES buffers, so STAGES-1 K steps of
+// loads are in flight while one is computed; one barrier per K step. LDS rows
+// are 128 bytes (64 bf16) with 16-byte chunk c of row r stored at c ^ rperm(r):
+// the 32x32x16 MFMA fragment reads (one chunk of 32 consecutive rows) are then
+// conflict-free, and each 64-lane load instruction still writes one
+// contiguous kilobyte of LDS as the direct-to-LDS path requires.
 //
 // For qkv_rope the MFMA "A" operand is the weight tile and "B" the token
 // tile, so the accumulator holds features down its rows: a lane then owns 4
@@ -22,15 +27,14 @@
 
 namespace gqa {
 
-constexpr int BK = 64;          // K step staged per iteration
-constexpr int GEMM_THREADS = 256;
+constexpr int BK = 64;  // K step
 
 enum Epilogue { EPI_QKV_ROPE = 0, EPI_OUT_F32 = 1 };
 
 struct GemmArgs {
   const uint16_t* act;   // [M][4096] bf16 activations
-  const uint16_t* w0;    // weight rows [0, n0_rows)
-  const uint16_t* w1;    // fused QKV: W_K rows; unused otherwise
+  const uint16_t* w0;    // weight rows (W_Q, or W_O)
+  const uint16_t* w1;    // fused QKV: W_K rows
   const uint16_t* w2;    // fused QKV: W_V rows
   int M;                 // tokens
   int N;                 // output features (6144 or 4096)
@@ -43,32 +47,39 @@ struct GemmArgs {
   float* out;            // [M][4096]
 };
 
-// LDS tile of R rows x 64 bf16: row r, 16-byte chunk c is stored at chunk c ^ (r & 7).
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ (r & 7)) << 3); }
+// Chunk permutation of row r: a bijection on r & 7 for any 8 aligned rows (so 8
+// lanes reading one chunk of rows r0..r0+7 hit 8 distinct 16-byte slots of a
+// 128-byte bank window), which also differs between rows r and r + 8 (so 16
+// lanes reading rows r0..r0+15 hit 16 distinct slots of a 256-byte window).
+__device__ __forceinline__ int rperm(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ rperm(r)) << 3); }
 
-template <int ROWS>
-__device__ __forceinline__ void load_tile(u32x4 (&reg)[ROWS * 8 / GEMM_THREADS],
-                                          const uint16_t* base, int rows_valid, int k0, int tid) {
-#pragma unroll
-  for (int c = 0; c < ROWS * 8 / GEMM_THREADS; ++c) {
-    int idx = c * GEMM_THREADS + tid;
-    int r = idx >> 3, ch = idx & 7;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (r < rows_valid) v = ld16(base + (size_t)r * D_MODEL + k0 + ch * 8);
-    reg[c] = v;
+// s_waitcnt with vmcnt(n) and the other counters left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Waits until at most n of this wave's K steps (PER load instructions each)
+// are still in flight; n <= MAXN, resolved to an immediate vmcnt.
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_keep(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<PER * MAXN>();
+    else wait_keep<PER, MAXN - 1>(n);
   }
 }
 
-template <int ROWS>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const u32x4 (&reg)[ROWS * 8 / GEMM_THREADS],
-                                           int tid) {
-#pragma unroll
-  for (int c = 0; c < ROWS * 8 / GEMM_THREADS; ++c) {
-    int idx = c * GEMM_THREADS + tid;
-    int r = idx >> 3, ch = idx & 7;
-    st16(lds + swz(r, ch), reg[c]);
-  }
-}
+// Workgroup barrier without the memory fence __syncthreads() carries: the
+// fence would wait for every outstanding load (vmcnt(0)), draining the
+// prefetched stages. LDS is only written by the direct-to-LDS loads here, and
+// each wave has already waited (wait_vmcnt) for its own loads of the step it
+// is about to read, so the bare barrier orders everything that matters. The
+// "memory" clobber keeps the compiler from moving LDS reads across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // Maps a linear workgroup id to (token tile, feature tile): workgroups are
 // dealt round-robin to the 8 XCDs, so ids are first regrouped so that each
@@ -89,21 +100,36 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_tok, int
   tf = r / gsz;
 }
 
-template <int TOK, int FEAT, int EPI>
-__global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
-  // P: MFMA A operand rows, Q: MFMA B operand rows.
-  constexpr bool SWAP = (EPI == EPI_QKV_ROPE);
-  constexpr int PR = SWAP ? FEAT : TOK;
-  constexpr int QR = SWAP ? TOK : FEAT;
-  constexpr int WP = PR / 2, WQ = QR / 2;
-  constexpr int NP = WP / 32, NQ = WQ / 32;
-  constexpr int LP = PR * BK, LQ = QR * BK;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (LP + LQ)];
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
+struct GemmCfg {
+  static constexpr bool SWAP = (EPI == EPI_QKV_ROPE);
+  static constexpr int PR = SWAP ? FEAT : TOK;   // MFMA A operand rows
+  static constexpr int QR = SWAP ? TOK : FEAT;   // MFMA B operand rows
+  static constexpr int NW = WPN * WQN;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int WP = PR / WPN, WQ = QR / WQN;   // wave tile
+  static constexpr int NP = WP / 32, NQ = WQ / 32;
+  static constexpr int STAGE_ELEMS = (PR + QR) * BK;
+  static constexpr int LDS_BYTES = STAGES * STAGE_ELEMS * 2;
+  static constexpr int NI = (PR + QR) / 8;             // 1 KiB load instructions per stage
+  static constexpr int NI_W = NI / NW;                 // per wave
+  static_assert(NI % NW == 0, "load instructions must split evenly across waves");
+  static_assert(WP % 32 == 0 && WQ % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
+};
+
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
+__global__ __launch_bounds__(64 * WPN * WQN)
+void gemm_nt_kernel(GemmArgs a) {
+  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI>;
+  constexpr int PR = C::PR, QR = C::QR, NP = C::NP, NQ = C::NQ;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * C::STAGE_ELEMS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wp = wave >> 1, wq = wave & 1;
+  const int wp = wave / WQN, wq = wave % WQN;
 
   const int tiles_tok = (a.M + TOK - 1) / TOK;
   const int tiles_feat = a.N / FEAT;
@@ -121,11 +147,34 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
     wbase = a.w0 + (size_t)n0 * D_MODEL;
   }
   const uint16_t* abase = a.act + (size_t)m0 * D_MODEL;
-  const int tok_valid = a.M - m0;
-  const uint16_t* pbase = SWAP ? wbase : abase;
-  const uint16_t* qbase = SWAP ? abase : wbase;
-  const int p_valid = SWAP ? PR : tok_valid;
-  const int q_valid = SWAP ? tok_valid : QR;
+  const int tok_last = a.M - m0 - 1;   // rows past it are clamped (their outputs are discarded)
+
+  // This lane's source pointers for its NI_W load instructions (K offset added per step).
+  // Instruction i covers LDS rows 8i..8i+7 of the stage (P rows first, then Q rows);
+  // lane l writes row 8i + (l >> 3), physical chunk l & 7 = logical chunk (l & 7) ^ rperm(row).
+  const uint16_t* src[C::NI_W];
+#pragma unroll
+  for (int j = 0; j < C::NI_W; ++j) {
+    const int i = wave + j * C::NW;
+    int row = 8 * i + (lane >> 3);
+    const int lc = (lane & 7) ^ rperm(row);
+    const bool is_p = row < PR;
+    const int r = is_p ? row : row - PR;
+    const bool is_tok = C::SWAP ? !is_p : is_p;
+    const int rr = is_tok ? min(r, tok_last) : r;
+    const uint16_t* base = C::SWAP ? (is_p ? wbase : abase) : (is_p ? abase : wbase);
+    src[j] = base + (size_t)rr * D_MODEL + lc * 8;
+  }
+  auto issue = [&](int kt, int stage) {
+#pragma unroll
+    for (int j = 0; j < C::NI_W; ++j) {
+      const int i = wave + j * C::NW;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(src[j] + kt * BK),
+          (__attribute__((address_space(3))) void*)(smem + stage * C::STAGE_ELEMS + i * 512),
+          16, 0, 0);
+    }
+  };
 
   f32x16 acc[NP][NQ];
 #pragma unroll
@@ -133,44 +182,43 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) acc[i][j] = f32x16{};
 
-  u32x4 preg[PR * 8 / GEMM_THREADS];
-  u32x4 qreg[QR * 8 / GEMM_THREADS];
-
-  load_tile<PR>(preg, pbase, p_valid, 0, tid);
-  load_tile<QR>(qreg, qbase, q_valid, 0, tid);
-  store_tile<PR>(smem, preg, tid);
-  store_tile<QR>(smem + LP, qreg, tid);
-  __syncthreads();
-
   constexpr int NK = D_MODEL / BK;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+
   const int lrow = lane & 31, lhalf = lane >> 5;
   for (int kt = 0; kt < NK; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < NK) {
-      load_tile<PR>(preg, pbase, p_valid, (kt + 1) * BK, tid);
-      load_tile<QR>(qreg, qbase, q_valid, (kt + 1) * BK, tid);
-    }
-    const uint16_t* sp = smem + cur * (LP + LQ);
-    const uint16_t* sq = sp + LP;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      u32x4 af[NP], bf[NQ];
+    // wait for this step's loads; keep the later steps' loads (at most STAGES-2) in flight
+    wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 1 - kt));
+    barrier_no_fence();
+    if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+
+    const uint16_t* sp = smem + (kt % STAGES) * C::STAGE_ELEMS;
+    const uint16_t* sq = sp + PR * BK;
+    // fragments double-buffered in registers: reads of slice kk+1 overlap the MFMAs of kk
+    u32x4 af[2][NP], bf[2][NQ];
+    auto read_frags = [&](int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
       const int ch = kk * 2 + lhalf;
 #pragma unroll
-      for (int i = 0; i < NP; ++i) af[i] = ld16(sp + swz(wp * WP + i * 32 + lrow, ch));
+      for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz(wp * C::WP + i * 32 + lrow, ch));
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) bf[j] = ld16(sq + swz(wq * WQ + j * 32 + lrow, ch));
+      for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz(wq * C::WQ + j * 32 + lrow, ch));
+    };
+    read_frags(0, af[0], bf[0]);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      // Issue the reads of slice kk+1 before the MFMAs of slice kk and keep the
+      // scheduler from reordering them (it would otherwise sink the reads behind
+      // the MFMAs and reuse one register set, exposing the LDS latency per slice).
+      if (kk + 1 < BK / 16) read_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < NP; ++i)
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) acc[i][j] = mfma_32x32x16(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < NQ; ++j)
+          acc[i][j] = mfma_32x32x16(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < NK) {
-      uint16_t* dp = smem + (cur ^ 1) * (LP + LQ);
-      store_tile<PR>(dp, preg, tid);
-      store_tile<QR>(dp + LP, qreg, tid);
-    }
-    __syncthreads();
   }
 
   if (EPI == EPI_QKV_ROPE) {
@@ -179,7 +227,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
     const int fbase = region == 0 ? 0 : (region == 1 ? D_MODEL : D_MODEL + N_KV * D_HEAD);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int tok = m0 + wq * WQ + j * 32 + lrow;
+      const int tok = m0 + wq * C::WQ + j * 32 + lrow;
       if (tok >= a.M) continue;
       const int b = tok / a.T;
       const int t = tok - b * a.T;
@@ -191,7 +239,7 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
       for (int i = 0; i < NP; ++i) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = n0 + wp * WP + i * 32 + 8 * g + 4 * lhalf - fbase;
+          const int f = n0 + wp * C::WP + i * 32 + 8 * g + 4 * lhalf - fbase;
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if (region != 2) {
@@ -214,9 +262,9 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
     for (int i = 0; i < NP; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int tok = m0 + wp * WP + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
+        const int tok = m0 + wp * C::WP + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         if (tok >= a.M) continue;
-        float* orow = a.out + (size_t)tok * D_MODEL + n0 + wq * WQ + lrow;
+        float* orow = a.out + (size_t)tok * D_MODEL + n0 + wq * C::WQ + lrow;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) orow[j * 32] = acc[i][j][r];
       }
@@ -224,13 +272,16 @@ __global__ __launch_bounds__(GEMM_THREADS) void gemm_nt_kernel(GemmArgs a) {
   }
 }
 
-template <int TOK, int FEAT, int EPI>
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI>;
   const int tiles = ((a.M + TOK - 1) / TOK) * (a.N / FEAT);
-  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, EPI>), dim3(tiles), dim3(GEMM_THREADS), 0, s, a);
+  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI>), dim3(tiles),
+                     dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
+#ifndef GQA_GEMM_NO_LAUNCHERS
 hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
@@ -241,14 +292,22 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
   a.rope = rope; a.T = T;
   a.q_dst = q_dst; a.q_bstride = q_bstride; a.q_rstride = q_rstride;
   a.k_dst = k_dst; a.v_dst = v_dst; a.kv_bstride = kv_bstride; a.kv_rstride = kv_rstride;
-  return launch_gemm<128, 128, EPI_QKV_ROPE>(a, s);
+  // Few tokens (decode): thin weight strips and a deep load ring, so the weights
+  // stream from HBM through many workgroups; otherwise the largest tile that
+  // still fills the chip.
+  if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
+  if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);
+  return launch_gemm<256, 256, 4, 2, 2, EPI_QKV_ROPE>(a, s);
 }
 
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
                            hipStream_t s) {
   GemmArgs a{};
   a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1;
-  return launch_gemm<128, 128, EPI_OUT_F32>(a, s);
+  if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
+  if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
+  return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
 }
+#endif
 
 }  // namespace gqa
