@@ -54,33 +54,6 @@ struct GemmArgs {
 __device__ __forceinline__ int rperm(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ rperm(r)) << 3); }
 
-// s_waitcnt with vmcnt(n) and the other counters left free (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-}
-
-// Waits until at most n of this wave's K steps (PER load instructions each)
-// are still in flight; n <= MAXN, resolved to an immediate vmcnt.
-template <int PER, int MAXN>
-__device__ __forceinline__ void wait_keep(int n) {
-  if constexpr (MAXN <= 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (n >= MAXN) wait_vmcnt<PER * MAXN>();
-    else wait_keep<PER, MAXN - 1>(n);
-  }
-}
-
-// Workgroup barrier without the memory fence __syncthreads() carries: the
-// fence would wait for every outstanding load (vmcnt(0)), draining the
-// prefetched stages. LDS is only written by the direct-to-LDS loads here, and
-// each wave has already waited (wait_vmcnt) for its own loads of the step it
-// is about to read, so the bare barrier orders everything that matters. The
-// "memory" clobber keeps the compiler from moving LDS reads across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
 // Maps a linear workgroup id to (token tile, feature tile): workgroups are
 // dealt round-robin to the 8 XCDs, so ids are first regrouped so that each
 // XCD owns a contiguous run of tiles, and runs are walked in groups of

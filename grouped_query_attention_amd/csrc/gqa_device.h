@@ -20,6 +20,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 // Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -45,6 +46,33 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
+
+// s_waitcnt with vmcnt(n) and the other counters left free (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Waits until at most n of this wave's K steps (PER load instructions each)
+// are still in flight; n <= MAXN, resolved to an immediate vmcnt.
+template <int PER, int MAXN>
+__device__ __forceinline__ void wait_keep(int n) {
+  if constexpr (MAXN <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAXN) wait_vmcnt<PER * MAXN>();
+    else wait_keep<PER, MAXN - 1>(n);
+  }
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries: the
+// fence would wait for every outstanding load (vmcnt(0)), draining prefetched
+// pipeline stages. Used where LDS is only written by direct-to-LDS loads and
+// each wave has already waited (wait_vmcnt / wait_keep) for its own loads of
+// the stage it is about to read. The "memory" clobber keeps the compiler from
+// moving LDS reads across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
