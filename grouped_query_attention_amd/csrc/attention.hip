@@ -8,22 +8,24 @@
 //
 // Prefill (flash_fwd_kernel): one workgroup per (64-position query tile, KV
 // head g, sequence b) runs 8 waves: wave w takes query head 4g + (w & 3) and
-// 32 of the 64 positions. Every 64-key tile of K_r and V is staged in LDS
-// once and used by all four heads of the group. Scores are computed
+// 32 of the 64 positions. Every 64-key tile of K_r and V is loaded into LDS
+// once (straight from HBM, through a 4-stage ring) and used by all four heads
+// of the group. Waves w and w+4 share a SIMD and are offset by half a tile, so
+// one's MFMAs run while the other computes its softmax. Scores are computed
 // transposed (keys down the MFMA rows, queries across the lanes), so each lane
-// owns one query: the running max and sum need only in-lane work plus one
-// swap with the lane 32 away, and the bf16 probabilities feed the P·V MFMA
-// straight from the score accumulator. V is transposed into LDS while being
-// staged, with the key order inside each 16-key group permuted to match the
-// accumulator layout. The softmax is the online (running max / running sum)
-// form in base 2 with log2(e)/sqrt(128) folded into one multiply-add; the
-// division by the row sum happens once, at the end, in fp32.
+// owns one query: the running max needs only in-lane work plus one swap with
+// the lane 32 away, and the bf16 probabilities feed the P·V MFMA straight from
+// the score accumulator. V is read with transposing LDS loads, in the key
+// order the accumulator holds. The softmax is the online (running max /
+// running sum) form in base 2 with log2(e)/sqrt(128) folded into one
+// multiply-add, with a lazily moved reference max; the division by the row sum
+// happens once, at the end, in fp32.
 //
 // Decode (decode_splitkv_kernel + decode_merge_kernel): the key range of each
-// (sequence, KV head) is split into chunks of 512 keys; a workgroup of 4 waves
-// takes one chunk (128 keys per wave) for the 4 query heads of the group,
-// combines its waves in LDS, and writes an unnormalised partial (max, sum,
-// O[4][128]); the merge kernel rescales and sums the partials.
+// sequence is split into chunks; persistent workgroups of 8 waves (one per KV
+// head) stream whole cache rows of their chunks through LDS and write one
+// unnormalised partial (max, sum, O[4][128]) per (chunk, KV head); the merge
+// kernel rescales and sums the partials.
 
 #include "gqa_device.h"
 #include "gqa_launch.h"
@@ -40,19 +42,36 @@ constexpr float NEG_INF = -__builtin_inff();
 // Prefill
 // ----------------------------------------------------------------------------
 
-constexpr int FA_BQ = 64;       // query positions per workgroup
-constexpr int FA_BN = 64;       // keys per staged tile
-constexpr int FA_THREADS = 512;
+constexpr int FA_BQ = 64;        // query positions per workgroup
+constexpr int FA_BN = 64;        // keys per staged tile
+constexpr int FA_THREADS = 512;  // 8 waves: 4 heads x 2 blocks of 32 positions
+constexpr int FA_STAGES = 4;     // K/V tiles resident: t-1 (V, lagging waves), t, t+1, t+2
+constexpr int FA_TILE = FA_BN * D_HEAD;   // elements of one K or V tile (16 KiB)
+constexpr int FA_NI_W = 4;       // 1-KiB direct-to-LDS loads per wave per tile (16 K + 16 V over 8 waves)
+// Lazy rescaling: the reference max of a row only moves when a score exceeds it
+// by 8 in base 2 (probabilities then stay <= 2^8), so the O rescale is skipped
+// for almost every tile. Expressed in raw-score units.
+constexpr float FA_RESCALE_RAW = 8.0f / SCALE_LOG2;
 
-// K tile: [64 keys][128 d]; 16-byte chunk c of key k at chunk c ^ (k & 15).
+// K tile [64 keys][128 d], 256-byte rows: 16-byte chunk c of key k at chunk
+// c ^ (k & 15), so the 16 lanes of a fragment read (16 keys, one chunk) hit 16
+// distinct slots.
 __device__ __forceinline__ int k_off(int key, int c) { return key * D_HEAD + ((c ^ (key & 15)) << 3); }
-// V^T tile: [128 d][64 key slots]; chunk c (8 slots) of row d at c ^ vsw(d).
-__device__ __forceinline__ int vsw(int d) { return (d & 7) ^ ((d >> 3) & 7); }
-__device__ __forceinline__ int vt_off(int d, int c) { return d * FA_BN + ((c ^ vsw(d)) << 3); }
-// Slot of key offset ko (0..15) inside its 16-key group: swaps keys 4..7 and 8..11
-// so that slot 8u + e holds key 8(e>>2) + 4u + (e&3), the key a lane of the
-// score accumulator holds in register e of that group.
-__device__ __forceinline__ int vslot(int ko) { return (((ko >> 2) & 1) << 3) | ((ko >> 3) << 2) | (ko & 3); }
+// V tile [64 keys][128 d], row-major: chunk c of key k at chunk c ^ 4(k & 3).
+// A transposed read covers 4 consecutive keys x 64 bytes per half-wave; the
+// permutation spreads those 4 rows over all 16 slots of a 256-byte window.
+__device__ __forceinline__ int v_off(int key, int c) { return key * D_HEAD + ((c ^ ((key & 3) << 2)) << 3); }
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_lds;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane s supplies the address of
+// 4 consecutive bf16 of row (s >> 2) of a 4-row block, columns 4(s & 3)..+3;
+// lane i receives column i of the 4 rows (one value per row).
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
+  bf16x4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4_lds*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 struct FlashArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
@@ -63,11 +82,14 @@ struct FlashArgs {
 };
 
 __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][FA_BN * D_HEAD];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][D_HEAD * FA_BN];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[FA_STAGES * 2 * FA_TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // Waves w and w+4 share a SIMD. The first four run each tile as QK -> softmax
+  // -> P·V; the other four run the P·V of the previous tile first, so on every
+  // SIMD one wave's MFMAs overlap the other's softmax between two barriers.
+  const bool lag = wave >= 4;
   const int g = blockIdx.x & (N_KV - 1);
   const int rest = blockIdx.x >> 3;
   const int b = rest % a.B;
@@ -77,8 +99,8 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   const int qi = q0 + (wave >> 2) * 32 + lrow;        // this lane's query index
   const int qpos = a.q_pos0 + qi;
 
-  const uint16_t* kb = a.k + b * a.kv_bstride + g * D_HEAD;
-  const uint16_t* vb = a.v + b * a.kv_bstride + g * D_HEAD;
+  const uint16_t* kbase = a.k + b * a.kv_bstride + g * D_HEAD;
+  const uint16_t* vbase = a.v + b * a.kv_bstride + g * D_HEAD;
 
   // Query fragments (MFMA B operand): k-step s covers d = 16s + 8*lhalf .. +7.
   u32x4 qf[8];
@@ -96,76 +118,55 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   if (a.causal) kv_end = min(kv_end, a.q_pos0 + q0 + FA_BQ);
   const int n_tiles = (kv_end + FA_BN - 1) / FA_BN;
 
-  // staging: K chunk (key kk, chunk kc) and a V key pair (2*vp, 2*vp+1) x chunk vc
-  u32x4 kr[2], vr[2];
-  auto gload = [&](int t) {
-    const int base = t * FA_BN;
+  // Direct-to-LDS loads of tile t: instruction i (0..31) covers rows 4(i&15)..+3
+  // of K (i < 16) or V; lane l writes row 4(i&15) + (l >> 4), physical chunk
+  // l & 15. Keys past the end are clamped to the last key (finite values; masked).
+  auto issue = [&](int t) {
+    uint16_t* st = smem + (t % FA_STAGES) * 2 * FA_TILE;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = c * FA_THREADS + tid;
-      const int key = idx >> 4, ch = idx & 15;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kr[c] = (base + key < a.kv_len) ? ld16(kb + (size_t)(base + key) * (N_KV * D_HEAD) + ch * 8) : z;
-    }
-    const int vp = tid >> 4, vc = tid & 15;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int key = base + 2 * vp + c;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      vr[c] = (key < a.kv_len) ? ld16(vb + (size_t)key * (N_KV * D_HEAD) + vc * 8) : z;
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = c * FA_THREADS + tid;
-      const int key = idx >> 4, ch = idx & 15;
-      st16(&sk[buf][k_off(key, ch)], kr[c]);
-    }
-    const int vp = tid >> 4, vc = tid & 15;
-    const int key = 2 * vp;
-    const int slot = (key & ~15) | vslot(key & 15);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t wa = vr[0][e >> 1];
-      const uint32_t wb = vr[1][e >> 1];
-      const uint32_t w = (e & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
-      const int d = vc * 8 + e;
-      *reinterpret_cast<uint32_t*>(&sv[buf][d * FA_BN + (((slot >> 3) ^ vsw(d)) << 3) + (slot & 7)]) = w;
+    for (int j = 0; j < FA_NI_W; ++j) {
+      const int i = wave + 8 * j;
+      const bool isv = i >= 16;
+      const int r = 4 * (i & 15) + (lane >> 4);
+      const int key = min(t * FA_BN + r, a.kv_len - 1);
+      const int lc = isv ? ((lane & 15) ^ ((r & 3) << 2)) : ((lane & 15) ^ (r & 15));
+      const uint16_t* src = (isv ? vbase : kbase) + (size_t)key * (N_KV * D_HEAD) + lc * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(st + (isv ? FA_TILE : 0) + (i & 15) * 512),
+          16, 0, 0);
     }
   };
 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_run = NEG_INF;   // running max, raw-score units
-  float l_run = 0.f;       // this lane's share of the running sum
+  float m_ref = NEG_INF;   // reference max of this lane's query row, raw-score units
+  float l_run = 0.f;       // this lane's share of the row sum (relative to m_ref)
+  u32x4 pf[4];             // bf16 probabilities of the last softmax (P^T fragments)
 
   const bool has_mask = a.mask != nullptr;
   const float* mrow = has_mask ? a.mask + (size_t)(qi < a.T ? qi : 0) * a.kv_len : nullptr;
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
-    const int k0 = t * FA_BN;
-
-    // S^T for two 32-key blocks: lane holds query lrow, keys 32kb + 8(i>>2) + 4*lhalf + (i&3)
+  // S^T = K·Q^T, then the online softmax of tile t, leaving P^T in pf.
+  auto qk_softmax = [&](int t) {
+    const uint16_t* sk = smem + (t % FA_STAGES) * 2 * FA_TILE;
+    // Two partial sums per 32-key block over alternate d steps: four independent
+    // accumulation chains, so no MFMA waits on the result of the one before it.
+    f32x16 sp[2][2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) sp[kb2][0] = sp[kb2][1] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+        sp[kb2][st & 1] = mfma_32x32x16(ld16(sk + k_off(kb2 * 32 + lrow, 2 * st + lhalf)), qf[st],
+                                        sp[kb2][st & 1]);
     f32x16 s[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      s[kb2] = f32x16{};
-      const int key = kb2 * 32 + lrow;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const u32x4 kf = ld16(&sk[cur][k_off(key, 2 * st + lhalf)]);
-        s[kb2] = mfma_32x32x16(kf, qf[st], s[kb2]);
-      }
-    }
-
+    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = sp[kb2][0] + sp[kb2][1];
+    // lane holds query lrow, keys 32kb + 8(i>>2) + 4*lhalf + (i&3)
+    const int k0 = t * FA_BN;
     const bool edge = (a.causal && (k0 + FA_BN - 1 > a.q_pos0 + q0)) || (k0 + FA_BN > a.kv_len) || has_mask;
     if (edge) {
 #pragma unroll
@@ -179,21 +180,25 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
           s[kb2][i] = x;
         }
     }
-
     float mx = NEG_INF;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == NEG_INF) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * SCALE_LOG2);
-    m_run = m_new;
-    const float moff = -m_use * SCALE_LOG2;
-
+    const bool need = mx > m_ref + FA_RESCALE_RAW;     // false when mx = -inf
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = need ? mx : m_ref;
+      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2);   // 0 from -inf
+      m_ref = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    }
+    const float moff = (m_ref == NEG_INF) ? 0.f : -m_ref * SCALE_LOG2;
     float lsum = 0.f;
-    u32x4 pf[4];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -207,24 +212,45 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
         pf[kb2 * 2 + hf] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                  pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
-    l_run = l_run * alpha + lsum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+    l_run += lsum;
+  };
 
-    // O^T[d][q] += V^T[d][keys] · P^T[keys][q]; k-step sg covers slots 16sg .. 16sg+15
+  // O^T[d][q] += V^T[d][keys] · P^T[keys][q] for tile t; group sg holds keys
+  // 16sg..16sg+15. V^T fragments come from two transposed reads: lane group
+  // (lane >> 4) = (key quad u = lane >> 5, d half); source lane s = lane & 15
+  // points at key 4u + (s >> 2) (+8 for the second read), d = 32db + 16*dhalf + 4(s & 3).
+  const int tr_key = 4 * lhalf + ((lane & 15) >> 2);
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto pv = [&](int t) {
+    const uint16_t* sv = smem + (t % FA_STAGES) * 2 * FA_TILE + FA_TILE;
 #pragma unroll
     for (int sg = 0; sg < 4; ++sg)
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const int d = db * 32 + lrow;
-        const u32x4 vf = ld16(&sv[cur][vt_off(d, 2 * sg + lhalf)]);
+        const uint16_t* p = sv + v_off(16 * sg + tr_key, (32 * db + tr_d) >> 3) + (tr_d & 7);
+        const u32x2 r1 = ld_tr(p);
+        const u32x2 r2 = ld_tr(p + 8 * D_HEAD);
+        const u32x4 vf = {r1[0], r1[1], r2[0], r2[1]};
         o[db] = mfma_32x32x16(vf, pf[sg], o[db]);
       }
+  };
 
-    if (t + 1 < n_tiles) sstore(cur ^ 1);
-    __syncthreads();
+  issue(0);
+  if (n_tiles > 1) issue(1);
+  // trip t: tile t is computed (the lagging waves finish tile t-1); one extra
+  // trip lets the lagging waves do the last P·V.
+  for (int t = 0; t <= n_tiles; ++t) {
+    // tile t resident (tile t+1 may still be in flight); every wave is past
+    // trip t-1, so stage (t+2)%4 — last read as tile t-2 — is free
+    if (t + 1 < n_tiles) wait_vmcnt<FA_NI_W>(); else wait_vmcnt<0>();
+    barrier_no_fence();
+    if (t + 2 < n_tiles) issue(t + 2);
+    if (!lag) {
+      if (t < n_tiles) { qk_softmax(t); pv(t); }
+    } else {
+      if (t > 0) pv(t - 1);
+      if (t < n_tiles) qk_softmax(t);
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -259,185 +285,179 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
 // Decode
 // ----------------------------------------------------------------------------
 
-constexpr int DC_CHUNK = 512;    // keys per workgroup
-constexpr int DC_WKEYS = 128;    // keys per wave
-constexpr int DC_THREADS = 256;
+constexpr int DC_BN = 16;        // keys per staged tile, all 8 KV heads (2 KiB rows)
+constexpr int DC_THREADS = 512;  // 8 waves: wave g handles KV head g
+constexpr int DC_STAGES = 2;     // one tile computed while the next loads
+constexpr int DC_ROW = N_KV * D_HEAD;        // 1024 elements per cache row
+constexpr int DC_TILE = DC_BN * DC_ROW;      // elements of one K or V tile (32 KiB)
+constexpr int DC_NI_W = 8;       // 1-KiB direct-to-LDS loads per wave per tile (32 K + 32 V over 8 waves)
 constexpr int DC_PART = N_REP * D_HEAD + 2 * N_REP;   // floats per partial: O[4][128], m[4], l[4]
+constexpr int DC_TARGET_ITEMS = 768;                  // (sequence, chunk) items per launch
 
-// Per-wave V^T block: [128 d][32 slots]; 16-byte chunk u of row d at u ^ ((d >> 1) & 3).
-__device__ __forceinline__ int dvt_off(int d, int u) { return d * 32 + ((u ^ ((d >> 1) & 3)) << 3); }
-
-// Orders this wave's LDS writes before its later LDS reads (and vice versa)
-// across lanes, without involving the other waves of the workgroup.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+// Number of key chunks per sequence: enough items to balance the persistent
+// workgroups, never chunks shorter than one tile. Monotone in kv_len.
+__host__ __device__ inline int decode_n_split(int B, int kv_len) {
+  const int tiles = (kv_len + DC_BN - 1) / DC_BN;
+  const int want = (DC_TARGET_ITEMS + B - 1) / B;
+  return want < 1 ? 1 : (want > tiles ? tiles : want);
 }
+
+// Tile layout: [16 keys][8 heads][128 d], 2 KiB rows as in the cache, so every
+// load reads whole contiguous rows. Inside each head's 256 bytes, K chunk c of
+// key k sits at c ^ k (16 keys per fragment read hit 16 slots) and V chunk c
+// at c ^ 2(k & 7) (a transposed read of 16 keys x 32 bytes covers each slot
+// pair twice).
+__device__ __forceinline__ int dk_off(int key, int g, int c) { return key * DC_ROW + g * D_HEAD + ((c ^ (key & 15)) << 3); }
+__device__ __forceinline__ int dv_off(int key, int g, int c) { return key * DC_ROW + g * D_HEAD + ((c ^ ((key & 7) << 1)) << 3); }
 
 struct DecodeArgs {
   const uint16_t* q; const uint16_t* kc; const uint16_t* vc;
   float* part; uint16_t* h;
-  int B, S_max, kv_len, n_split;
+  int B, S_max, kv_len, n_split, chunk;   // chunk: keys per item (multiple of DC_BN)
+  int n_items;
 };
 
+// Persistent split-KV decode. Item j = (sequence b, chunk sp) covers keys
+// [sp*chunk, min(kv_len, (sp+1)*chunk)) of all 8 KV heads. Workgroup w takes
+// items w, w+G, w+2G, ... and streams their 16-key tiles of whole cache rows
+// HBM -> LDS as one continuous sequence (the next tile always loading while one
+// is computed, across item boundaries). Wave g owns KV head g and its 4 query
+// heads: scores S^T[16 keys][16 columns] from 16x16x32 MFMAs whose columns are
+// the 4 query heads (the other 12 are zero), so a lane of the accumulator holds
+// 4 keys of one head — exactly the P^T operand of the 16x16x16 P·V MFMA, whose
+// V^T operand is one transposed LDS read. Online softmax with a lazily moved
+// reference max; each wave writes an unnormalised fp32 partial per item.
 __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t svt[4][D_HEAD * 32];
-  __shared__ float s_o[4][N_REP][D_HEAD];
-  __shared__ float s_ml[4][2][N_REP];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int g = blockIdx.x & (N_KV - 1);
-  const int rest = blockIdx.x >> 3;
-  const int sp = rest % a.n_split;
-  const int b = rest / a.n_split;
+  const int G = gridDim.x;
 
-  const size_t row_stride = N_KV * D_HEAD;
-  const uint16_t* kbase = a.kc + (size_t)b * a.S_max * row_stride + g * D_HEAD;
-  const uint16_t* vbase = a.vc + (size_t)b * a.S_max * row_stride + g * D_HEAD;
+  auto item_tiles = [&](int item) {
+    const int k0 = (item % a.n_split) * a.chunk;
+    return (min(a.kv_len - k0, a.chunk) + DC_BN - 1) / DC_BN;
+  };
+  const int my_items = (a.n_items - (int)blockIdx.x + G - 1) / G;
 
-  // Query fragments (MFMA B operand, 16x16x32): column l16 = query head 4g + l16 (valid < 4),
-  // k-step s covers d = 32s + 8*lg .. +7.
-  u32x4 qf[4];
-  {
-    const bool ok = l16 < N_REP;
-    const uint16_t* qrow = a.q + ((size_t)b * N_HEADS + g * N_REP + (ok ? l16 : 0)) * D_HEAD + 8 * lg;
+  // load cursor over this workgroup's tiles: (item index j, tile t)
+  int ld_j = 0, ld_t = 0, ld_n = 0, stage_ld = 0;
+  auto issue_next = [&]() {
+    const int item = blockIdx.x + ld_j * G;
+    const int b = item / a.n_split;
+    const int key_t = (item % a.n_split) * a.chunk + ld_t * DC_BN;
+    const size_t seq = (size_t)b * a.S_max * DC_ROW;
+    uint16_t* st = smem + stage_ld * 2 * DC_TILE;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[s] = ok ? ld16(qrow + 32 * s) : z;
+    for (int j = 0; j < DC_NI_W; ++j) {
+      // instruction i (0..63): half a row — rows i>>1 of K (i < 32) or V
+      const int i = g + 8 * j;
+      const bool isv = i >= 32;
+      const int ii = i & 31;
+      const int r = ii >> 1;
+      const int p = (ii & 1) * 64 + lane;          // physical 16-byte chunk in the row
+      const int hg = p >> 4, pc = p & 15;
+      const int lc = isv ? (pc ^ ((r & 7) << 1)) : (pc ^ (r & 15));
+      const int key = min(key_t + r, a.kv_len - 1);   // clamped keys are masked below
+      const uint16_t* src = (isv ? a.vc : a.kc) + seq + (size_t)key * DC_ROW + hg * D_HEAD + lc * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const void*)src,
+          (__attribute__((address_space(3))) void*)(st + (isv ? DC_TILE : 0) + ii * 512),
+          16, 0, 0);
     }
-  }
+    stage_ld ^= 1;
+    if (++ld_t == ld_n) { ld_t = 0; ++ld_j; if (ld_j < my_items) ld_n = item_tiles(blockIdx.x + ld_j * G); }
+  };
+  int total_tiles = 0;
+  for (int j = 0; j < my_items; ++j) total_tiles += item_tiles(blockIdx.x + j * G);
+  if (my_items > 0) ld_n = item_tiles(blockIdx.x);
+  int issued = 0;
+  if (issued < total_tiles) { issue_next(); ++issued; }
 
-  f32x4 o[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = f32x4{};
-  float m_run = NEG_INF, l_run = 0.f;
+  int done = 0;
+  for (int j = 0; j < my_items; ++j) {
+    const int item = blockIdx.x + j * G;
+    const int sp = item % a.n_split;
+    const int b = item / a.n_split;
+    const int nt = item_tiles(item);
 
-  const int wk0 = sp * DC_CHUNK + wave * DC_WKEYS;
-  uint16_t* vt = svt[wave];
-
-  for (int blk = 0; blk < DC_WKEYS / 32; ++blk) {
-    const int kbeg = wk0 + blk * 32;
-    if (kbeg >= a.kv_len) break;                      // wave-uniform
-    // K fragments: sub-block kb2 (16 keys), k-step s: key kbeg + 16kb2 + l16, chunk 4s + lg
-    u32x4 kf[2][4];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      const int key = kbeg + 16 * kb2 + l16;
-      const bool ok = key < a.kv_len;
+    // Query fragments (MFMA B operand, 16x16x32): column l16 = query head 4g + l16
+    // (zero for l16 >= 4), k-step s covers d = 32s + 8*lg .. +7.
+    u32x4 qf[4];
+    {
+      const bool ok = l16 < N_REP;
+      const uint16_t* qrow = a.q + ((size_t)b * N_HEADS + g * N_REP + (ok ? l16 : 0)) * D_HEAD + 8 * lg;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 z = {0u, 0u, 0u, 0u};
-        kf[kb2][s] = ok ? ld16(kbase + (size_t)key * row_stride + 32 * s + 8 * lg) : z;
+        qf[s] = ok ? ld16(qrow + 32 * s) : z;
       }
     }
-    // V rows: load j = 4r + c covers key kbeg + 16r + 4lg + c, chunk l16
-    u32x4 vr[8];
+    f32x4 o[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = kbeg + 16 * (j >> 2) + 4 * lg + (j & 3);
-      u32x4 z = {0u, 0u, 0u, 0u};
-      vr[j] = key < a.kv_len ? ld16(vbase + (size_t)key * row_stride + 8 * l16) : z;
-    }
+    for (int i = 0; i < 8; ++i) o[i] = f32x4{};
+    float m_ref = NEG_INF, l_run = 0.f;
 
-    f32x4 sacc[2];
+    for (int t = 0; t < nt; ++t, ++done) {
+      // tile `done` resident and every wave is past tile done-1, whose stage the next load reuses
+      wait_vmcnt<0>();
+      barrier_no_fence();
+      if (issued < total_tiles) { issue_next(); ++issued; }
+
+      const uint16_t* sk = smem + (done & 1) * 2 * DC_TILE;
+      const uint16_t* sv = sk + DC_TILE;
+      // S^T: lane holds query l16, keys 4lg + i of this tile
+      f32x4 sacc = f32x4{};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      sacc[kb2] = f32x4{};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) sacc[kb2] = mfma_16x16x32(kf[kb2][s], qf[s], sacc[kb2]);
-    }
-    // lane holds query l16, keys kbeg + 16kb2 + 4lg + i
-    float mx = NEG_INF;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int s = 0; s < 4; ++s)
+        sacc = mfma_16x16x32(ld16(sk + dk_off(l16, g, 4 * s + lg)), qf[s], sacc);
+      const int kb = sp * a.chunk + t * DC_BN + 4 * lg;
+      float mx = NEG_INF;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = kbeg + 16 * kb2 + 4 * lg + i;
-        if (key >= a.kv_len) sacc[kb2][i] = NEG_INF;
-        mx = fmaxf(mx, sacc[kb2][i]);
+        if (kb + i >= a.kv_len) sacc[i] = NEG_INF;
+        mx = fmaxf(mx, sacc[i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);              // finite: key kbeg is valid
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * SCALE_LOG2);
-    m_run = m_new;
-    const float moff = -m_new * SCALE_LOG2;
-    float p[8];
-    float lsum = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m_ref + FA_RESCALE_RAW;     // false when mx = -inf
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = need ? mx : m_ref;
+        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2);
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e >> 2][e & 3], SCALE_LOG2, moff));
-      lsum += p[e];
-    }
-    l_run = l_run * alpha + lsum;
-    // P^T fragment: slot 8lg + e holds key 16(e>>2) + 4lg + (e&3)
-    const u32x4 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-
-    // V^T into this wave's LDS block: key 16r + 4lg + c -> slot 8lg + 4r + c
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w0 = vr[4 * r + 0][e >> 1], w1 = vr[4 * r + 1][e >> 1];
-        const uint32_t w2 = vr[4 * r + 2][e >> 1], w3 = vr[4 * r + 3][e >> 1];
-        u32x2 w;
-        if (e & 1) {
-          w[0] = (w0 >> 16) | (w1 & 0xffff0000u);
-          w[1] = (w2 >> 16) | (w3 & 0xffff0000u);
-        } else {
-          w[0] = (w0 & 0xffffu) | (w1 << 16);
-          w[1] = (w2 & 0xffffu) | (w3 << 16);
-        }
-        const int d = 8 * l16 + e;
-        *reinterpret_cast<u32x2*>(vt + dvt_off(d, lg) + 4 * r) = w;
+        for (int i = 0; i < 8; ++i) o[i] *= alpha;
       }
-    wave_lds_sync();   // the transposed block is written by other lanes of this wave
-
+      const float moff = (m_ref == NEG_INF) ? 0.f : -m_ref * SCALE_LOG2;
+      float p[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], SCALE_LOG2, moff));
+        l_run += p[i];
+      }
+      const u32x2 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      // O^T[d][q] += V^T[d][keys] · P^T[keys][q] in 8 blocks of 16 d: a transposed
+      // read gives lane l the values V[4lg + e][16db + l16], e = 0..3.
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const u32x4 vf = ld16(vt + dvt_off(16 * db + l16, lg));
-      o[db] = mfma_16x16x32(vf, pf, o[db]);
+      for (int db = 0; db < 8; ++db) {
+        const int d = 16 * db + 4 * (l16 & 3);
+        const u32x2 vf = ld_tr(sv + dv_off(4 * lg + (l16 >> 2), g, d >> 3) + (d & 7));
+        o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vf),
+                                                           __builtin_bit_cast(i16x4, pf), o[db], 0, 0, 0);
+      }
     }
-    wave_lds_sync();   // all reads of the block done before the next block overwrites it
-  }
 
-  // wave totals: sum over the 4 lane groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  // o[db][i]: query l16, d = 16db + 4lg + i
-  if (l16 < N_REP) {
+    // this wave's partial for (b, g, sp): o[db][i] is query l16, d = 16db + 4lg + i
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    float* part = a.part + ((size_t)(b * N_KV + g) * a.n_split + sp) * DC_PART;
+    if (l16 < N_REP) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_o[wave][l16][16 * db + 4 * lg + i] = o[db][i];
-    if (lg == 0) { s_ml[wave][0][l16] = m_run; s_ml[wave][1][l16] = l_run; }
-  }
-  __syncthreads();
-
-  float* part = a.part + ((size_t)(b * N_KV + g) * a.n_split + sp) * DC_PART;
-#pragma unroll
-  for (int rep = 0; rep < 2; ++rep) {
-    const int idx = rep * DC_THREADS + tid;        // 0..511 = query * 128 + d
-    const int q = idx >> 7, d = idx & 127;
-    float M = NEG_INF;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][0][q]);
-    float acc = 0.f, L = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = s_ml[w][0][q];
-      const float f = mw == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((mw - M) * SCALE_LOG2);
-      acc += s_o[w][q][d] * f;
-      L += s_ml[w][1][q] * f;
+      for (int db = 0; db < 8; ++db)
+        *reinterpret_cast<f32x4*>(part + l16 * D_HEAD + 16 * db + 4 * lg) = o[db];
+      if (lg == 0) { part[N_REP * D_HEAD + l16] = m_ref; part[N_REP * D_HEAD + N_REP + l16] = l_run; }
     }
-    part[q * D_HEAD + d] = acc;
-    if (d == 0) { part[N_REP * D_HEAD + q] = M; part[N_REP * D_HEAD + N_REP + q] = L; }
   }
 }
 
@@ -464,18 +484,29 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
 }
 
 size_t decode_partials_bytes(int B, int S_max) {
-  const size_t n_split = (size_t)(S_max + DC_CHUNK - 1) / DC_CHUNK;
-  return (size_t)B * N_KV * n_split * DC_PART * sizeof(float);
+  return (size_t)B * N_KV * decode_n_split(B, S_max) * DC_PART * sizeof(float);
 }
 
 hipError_t launch_decode_attention(const uint16_t* q_r, const uint16_t* k_cache,
                                    const uint16_t* v_cache, int B, int S_max, int kv_len,
                                    float* partials, uint16_t* h_out, hipStream_t s) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n_cu <= 0)
+      n_cu = 256;
+  }
   DecodeArgs a{};
   a.q = q_r; a.kc = k_cache; a.vc = v_cache; a.part = partials; a.h = h_out;
   a.B = B; a.S_max = S_max; a.kv_len = kv_len;
-  a.n_split = (kv_len + DC_CHUNK - 1) / DC_CHUNK;
-  const long long grid = (long long)B * N_KV * a.n_split;
+  a.n_split = decode_n_split(B, kv_len);
+  const int tiles = (kv_len + DC_BN - 1) / DC_BN;
+  a.chunk = ((tiles + a.n_split - 1) / a.n_split) * DC_BN;
+  a.n_split = (kv_len + a.chunk - 1) / a.chunk;        // drop empty chunks
+  a.n_items = B * a.n_split;
+  const int grid = a.n_items < n_cu ? a.n_items : n_cu;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3((unsigned)grid), dim3(DC_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
