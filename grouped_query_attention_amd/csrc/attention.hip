@@ -102,17 +102,7 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   const uint16_t* kbase = a.k + b * a.kv_bstride + g * D_HEAD;
   const uint16_t* vbase = a.v + b * a.kv_bstride + g * D_HEAD;
 
-  // Query fragments (MFMA B operand): k-step s covers d = 16s + 8*lhalf .. +7.
   u32x4 qf[8];
-  {
-    const bool ok = qi < a.T;
-    const uint16_t* qrow = a.q + ((size_t)(b * a.T + (ok ? qi : 0)) * N_HEADS + h) * D_HEAD + 8 * lhalf;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qf[s] = ok ? ld16(qrow + 16 * s) : z;
-    }
-  }
 
   int kv_end = a.kv_len;
   if (a.causal) kv_end = min(kv_end, a.q_pos0 + q0 + FA_BQ);
@@ -131,10 +121,7 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
       const int key = min(t * FA_BN + r, a.kv_len - 1);
       const int lc = isv ? ((lane & 15) ^ ((r & 3) << 2)) : ((lane & 15) ^ (r & 15));
       const uint16_t* src = (isv ? vbase : kbase) + (size_t)key * (N_KV * D_HEAD) + lc * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(st + (isv ? FA_TILE : 0) + (i & 15) * 512),
-          16, 0, 0);
+      dma16((const void*)src, (st + (isv ? FA_TILE : 0) + (i & 15) * 512));
     }
   };
 
@@ -237,6 +224,21 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
 
   issue(0);
   if (n_tiles > 1) issue(1);
+  // Query fragments (MFMA B operand): k-step s covers d = 16s + 8*lhalf .. +7.
+  {
+    const bool ok = qi < a.T;
+    const uint16_t* qrow = a.q + ((size_t)(b * a.T + (ok ? qi : 0)) * N_HEADS + h) * D_HEAD + 8 * lhalf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qf[s] = ok ? ld16(qrow + 16 * s) : z;
+    }
+  }
+
+  // Wait for the query loads (and the first tiles) before the loop: vmcnt is one
+  // in-order counter, and with the query registers known complete here the
+  // compiler adds no wait of its own inside the loop.
+  wait_vmcnt<0>();
   // trip t: tile t is computed (the lagging waves finish tile t-1); one extra
   // trip lets the lagging waves do the last P·V.
   for (int t = 0; t <= n_tiles; ++t) {
@@ -285,12 +287,21 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
 // Decode
 // ----------------------------------------------------------------------------
 
-constexpr int DC_BN = 16;        // keys per staged tile, all 8 KV heads (2 KiB rows)
-constexpr int DC_THREADS = 512;  // 8 waves: wave g handles KV head g
-constexpr int DC_STAGES = 2;     // one tile computed while the next loads
+constexpr int DC_BN = 16;        // keys per staged tile
+#ifndef GQA_DECODE_HEADS
+#define GQA_DECODE_HEADS 4
+#endif
+constexpr int DC_HG = GQA_DECODE_HEADS;   // KV heads per workgroup (a slice of each 2 KiB cache row)
+constexpr int DC_THREADS = 64 * DC_HG;   // wave w handles KV head DC_HG * slice + w
+#ifndef GQA_DECODE_STAGES
+#define GQA_DECODE_STAGES (16 / GQA_DECODE_HEADS)
+#endif
+constexpr int DC_STAGES = GQA_DECODE_STAGES;   // tiles in the LDS ring
 constexpr int DC_ROW = N_KV * D_HEAD;        // 1024 elements per cache row
-constexpr int DC_TILE = DC_BN * DC_ROW;      // elements of one K or V tile (32 KiB)
-constexpr int DC_NI_W = 8;       // 1-KiB direct-to-LDS loads per wave per tile (32 K + 32 V over 8 waves)
+constexpr int DC_TROW = DC_HG * D_HEAD;      // elements per tile row (the workgroup's heads)
+constexpr int DC_TILE = DC_BN * DC_TROW;     // elements of one K or V tile (16 KiB)
+constexpr int DC_NI = DC_TILE / 512;         // 1-KiB loads per K or V tile
+constexpr int DC_NI_W = 2 * DC_NI / DC_HG;   // 1-KiB direct-to-LDS loads per wave per tile
 constexpr int DC_PART = N_REP * D_HEAD + 2 * N_REP;   // floats per partial: O[4][128], m[4], l[4]
 constexpr int DC_TARGET_ITEMS = 768;                  // (sequence, chunk) items per launch
 
@@ -298,17 +309,17 @@ constexpr int DC_TARGET_ITEMS = 768;                  // (sequence, chunk) items
 // workgroups, never chunks shorter than one tile. Monotone in kv_len.
 __host__ __device__ inline int decode_n_split(int B, int kv_len) {
   const int tiles = (kv_len + DC_BN - 1) / DC_BN;
-  const int want = (DC_TARGET_ITEMS + B - 1) / B;
+  const int want = (DC_TARGET_ITEMS + B * (N_KV / DC_HG) - 1) / (B * (N_KV / DC_HG));
   return want < 1 ? 1 : (want > tiles ? tiles : want);
 }
 
-// Tile layout: [16 keys][8 heads][128 d], 2 KiB rows as in the cache, so every
-// load reads whole contiguous rows. Inside each head's 256 bytes, K chunk c of
+// Tile layout: [16 keys][4 heads][128 d]: each load reads 1 KiB of contiguous
+// cache row (the workgroup's 4 heads). Inside each head's 256 bytes, K chunk c of
 // key k sits at c ^ k (16 keys per fragment read hit 16 slots) and V chunk c
 // at c ^ 2(k & 7) (a transposed read of 16 keys x 32 bytes covers each slot
 // pair twice).
-__device__ __forceinline__ int dk_off(int key, int g, int c) { return key * DC_ROW + g * D_HEAD + ((c ^ (key & 15)) << 3); }
-__device__ __forceinline__ int dv_off(int key, int g, int c) { return key * DC_ROW + g * D_HEAD + ((c ^ ((key & 7) << 1)) << 3); }
+__device__ __forceinline__ int dk_off(int key, int w, int c) { return key * DC_TROW + w * D_HEAD + ((c ^ (key & 15)) << 3); }
+__device__ __forceinline__ int dv_off(int key, int w, int c) { return key * DC_TROW + w * D_HEAD + ((c ^ ((key & 7) << 1)) << 3); }
 
 struct DecodeArgs {
   const uint16_t* q; const uint16_t* kc; const uint16_t* vc;
@@ -330,10 +341,15 @@ struct DecodeArgs {
 __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, g = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
   const int G = gridDim.x;
+  // cache bases as values: selecting between fields of the argument struct per
+  // lane makes the compiler load the pointer from memory with a vector load
+  const uint16_t* const kcache = a.kc;
+  const uint16_t* const vcache = a.vc;
 
+  // item = (sequence b, head half hh, chunk sp) = ((b * 2 + hh) * n_split + sp)
   auto item_tiles = [&](int item) {
     const int k0 = (item % a.n_split) * a.chunk;
     return (min(a.kv_len - k0, a.chunk) + DC_BN - 1) / DC_BN;
@@ -344,41 +360,43 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
   int ld_j = 0, ld_t = 0, ld_n = 0, stage_ld = 0;
   auto issue_next = [&]() {
     const int item = blockIdx.x + ld_j * G;
-    const int b = item / a.n_split;
+    const int bh = item / a.n_split;               // b * (8 / DC_HG) + head slice
     const int key_t = (item % a.n_split) * a.chunk + ld_t * DC_BN;
-    const size_t seq = (size_t)b * a.S_max * DC_ROW;
+    const size_t seq = (size_t)(bh / (N_KV / DC_HG)) * a.S_max * DC_ROW + (bh % (N_KV / DC_HG)) * DC_TROW;
     uint16_t* st = smem + stage_ld * 2 * DC_TILE;
 #pragma unroll
     for (int j = 0; j < DC_NI_W; ++j) {
-      // instruction i (0..63): half a row — rows i>>1 of K (i < 32) or V
-      const int i = g + 8 * j;
-      const bool isv = i >= 32;
-      const int ii = i & 31;
-      const int r = ii >> 1;
-      const int p = (ii & 1) * 64 + lane;          // physical 16-byte chunk in the row
-      const int hg = p >> 4, pc = p & 15;
+      // instruction i: the 1-KiB piece ii of the K (i < DC_NI) or V tile; lane l
+      // fills tile elements ii*512 + 8l .. +7: row r, head hg, physical chunk pc
+      const int i = w + DC_HG * j;
+      const bool isv = i >= DC_NI;
+      const int ii = i % DC_NI;
+      const int e = ii * 512 + lane * 8;
+      const int r = e / DC_TROW, col = e % DC_TROW;
+      const int hg = col >> 7, pc = (col >> 3) & 15;
       const int lc = isv ? (pc ^ ((r & 7) << 1)) : (pc ^ (r & 15));
       const int key = min(key_t + r, a.kv_len - 1);   // clamped keys are masked below
-      const uint16_t* src = (isv ? a.vc : a.kc) + seq + (size_t)key * DC_ROW + hg * D_HEAD + lc * 8;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)src,
-          (__attribute__((address_space(3))) void*)(st + (isv ? DC_TILE : 0) + ii * 512),
-          16, 0, 0);
+      const uint16_t* src = (isv ? vcache : kcache) + seq + (size_t)key * DC_ROW + hg * D_HEAD + lc * 8;
+      dma16((const void*)src, (st + (isv ? DC_TILE : 0) + ii * 512));
     }
-    stage_ld ^= 1;
+    stage_ld = (stage_ld + 1) % DC_STAGES;
     if (++ld_t == ld_n) { ld_t = 0; ++ld_j; if (ld_j < my_items) ld_n = item_tiles(blockIdx.x + ld_j * G); }
   };
   int total_tiles = 0;
   for (int j = 0; j < my_items; ++j) total_tiles += item_tiles(blockIdx.x + j * G);
   if (my_items > 0) ld_n = item_tiles(blockIdx.x);
   int issued = 0;
-  if (issued < total_tiles) { issue_next(); ++issued; }
+#pragma unroll
+  for (int s = 0; s < DC_STAGES - 1; ++s)
+    if (issued < total_tiles) { issue_next(); ++issued; }
 
   int done = 0;
   for (int j = 0; j < my_items; ++j) {
     const int item = blockIdx.x + j * G;
     const int sp = item % a.n_split;
-    const int b = item / a.n_split;
+    const int bh = item / a.n_split;
+    const int b = bh / (N_KV / DC_HG);
+    const int g = (bh % (N_KV / DC_HG)) * DC_HG + w;   // this wave's KV head
     const int nt = item_tiles(item);
 
     // Query fragments (MFMA B operand, 16x16x32): column l16 = query head 4g + l16
@@ -393,24 +411,29 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
         qf[s] = ok ? ld16(qrow + 32 * s) : z;
       }
     }
+    // vmcnt is one in-order counter shared with the direct-to-LDS stream: wait for
+    // the query loads here, once per item, or the compiler waits for every load in
+    // flight before the first use of qf in each tile.
+    wait_vmcnt<0>();
     f32x4 o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4{};
     float m_ref = NEG_INF, l_run = 0.f;
 
     for (int t = 0; t < nt; ++t, ++done) {
-      // tile `done` resident and every wave is past tile done-1, whose stage the next load reuses
-      wait_vmcnt<0>();
+      // tile `done` resident (later issued tiles may still load); every wave is past
+      // tile done-1, whose stage the next load reuses
+      wait_keep<DC_NI_W, DC_STAGES - 2>(min(DC_STAGES - 2, issued - done - 1));
       barrier_no_fence();
       if (issued < total_tiles) { issue_next(); ++issued; }
 
-      const uint16_t* sk = smem + (done & 1) * 2 * DC_TILE;
+      const uint16_t* sk = smem + (done % DC_STAGES) * 2 * DC_TILE;
       const uint16_t* sv = sk + DC_TILE;
       // S^T: lane holds query l16, keys 4lg + i of this tile
       f32x4 sacc = f32x4{};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        sacc = mfma_16x16x32(ld16(sk + dk_off(l16, g, 4 * s + lg)), qf[s], sacc);
+        sacc = mfma_16x16x32(ld16(sk + dk_off(l16, w, 4 * s + lg)), qf[s], sacc);
       const int kb = sp * a.chunk + t * DC_BN + 4 * lg;
       float mx = NEG_INF;
 #pragma unroll
@@ -442,7 +465,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const int d = 16 * db + 4 * (l16 & 3);
-        const u32x2 vf = ld_tr(sv + dv_off(4 * lg + (l16 >> 2), g, d >> 3) + (d & 7));
+        const u32x2 vf = ld_tr(sv + dv_off(4 * lg + (l16 >> 2), w, d >> 3) + (d & 7));
         o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, vf),
                                                            __builtin_bit_cast(i16x4, pf), o[db], 0, 0, 0);
       }
@@ -505,7 +528,7 @@ hipError_t launch_decode_attention(const uint16_t* q_r, const uint16_t* k_cache,
   const int tiles = (kv_len + DC_BN - 1) / DC_BN;
   a.chunk = ((tiles + a.n_split - 1) / a.n_split) * DC_BN;
   a.n_split = (kv_len + a.chunk - 1) / a.chunk;        // drop empty chunks
-  a.n_items = B * a.n_split;
+  a.n_items = B * (N_KV / DC_HG) * a.n_split;
   const int grid = a.n_items < n_cu ? a.n_items : n_cu;
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3((unsigned)grid), dim3(DC_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();

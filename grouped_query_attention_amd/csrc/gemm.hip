@@ -142,10 +142,7 @@ void gemm_nt_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < C::NI_W; ++j) {
       const int i = wave + j * C::NW;
-      __builtin_amdgcn_global_load_lds(
-          (const void*)(src[j] + kt * BK),
-          (__attribute__((address_space(3))) void*)(smem + stage * C::STAGE_ELEMS + i * 512),
-          16, 0, 0);
+      dma16((const void*)(src[j] + kt * BK), (smem + stage * C::STAGE_ELEMS + i * 512));
     }
   };
 

@@ -66,6 +66,21 @@ __device__ __forceinline__ void wait_keep(int n) {
   }
 }
 
+// 16-byte-per-lane direct-to-LDS load (global_load_lds_dwordx4): lane l's 16
+// bytes from `src` land at LDS byte lds_dst + 16*l (lds_dst wave-uniform). It is
+// issued through inline asm so that the compiler's wait-count pass does not see
+// it: that pass cannot count these loads across loop iterations and would
+// otherwise wait for every load in flight (vmcnt(0)) before the next use of any
+// register loaded from memory, or before LDS reads it cannot disambiguate,
+// draining the prefetch ring every step. The kernels issue their own waits
+// (wait_vmcnt / wait_keep) before a stage is read. M0 is written here and used
+// by nothing else in these kernels (a test checks the generated assembly).
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst;
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+}
+
 // Workgroup barrier without the memory fence __syncthreads() carries: the
 // fence would wait for every outstanding load (vmcnt(0)), draining prefetched
 // pipeline stages. Used where LDS is only written by direct-to-LDS loads and
