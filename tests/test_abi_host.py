@@ -67,7 +67,13 @@ def test_workspace_sizes():
     want = sum(((M * f * 2 + 255) // 256) * 256 for f in (4096, 1024, 1024, 4096))
     assert gqa.prefill_workspace_bytes(3, 129) == want
     assert gqa.prefill_workspace_bytes(0, 5) == 0
-    assert gqa.decode_workspace_bytes(64, 8192) > 64 * 8 * 16 * (4 * 130) * 4
+    # decode: Q_r and H (bf16 [B][4096] each) plus at least one fp32 partial
+    # (O[4][128], max[4], sum[4]) per (sequence, KV head); more keys never need less
+    for B in (1, 3, 64):
+        need = 2 * B * 4096 * 2 + B * 8 * (4 * 128 + 8) * 4
+        sizes = [gqa.decode_workspace_bytes(B, S) for S in (1, 64, 1000, 8192, 131072)]
+        assert all(sz >= need for sz in sizes)
+        assert sizes == sorted(sizes)
     assert gqa.decode_workspace_bytes(0, 10) == 0
 
 
