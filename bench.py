@@ -15,6 +15,7 @@ time in the headline step, timed with HIP events on the stream it runs on;
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+       python bench.py --only decode|prefill_B8_T4096|prefill_B1_T131072
 """
 
 import argparse
@@ -53,43 +54,25 @@ def decode_bytes(B, kv_len):
             + B * 4096 * 2 + B * 4096 * 4 + 64 * 2 * 4)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--quick", action="store_true", help="headline workload only")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
-                    help="only run a plain device copy of MB mebibytes (3 times), for "
-                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}))
-        sys.exit(2)
+class Bench:
+    def __init__(self, args):
+        import torch
+        import gqa_inputs as gi
+        import grouped_query_attention_amd as gqa
+        self.torch, self.gi, self.gqa = torch, gi, gqa
+        self.args = args
+        self.dev = torch.device("cuda:0")
 
-    import torch
-    import gqa_inputs as gi
-    import grouped_query_attention_amd as gqa
+    @staticmethod
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
 
-    dev = torch.device("cuda:0")
-    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    def up(self, bits):
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.to(self.dev).view(self.torch.bfloat16)
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": n, "launches": 3}))
-        return
-
-    def up(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    def time_steps(fn, steps, warmup):
+    def time_steps(self, fn, steps, warmup):
+        torch = self.torch
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -105,79 +88,83 @@ def main():
         return e0.elapsed_time(e1) / steps, wall
 
     # ---------------- headline: prefill B=1 T=2048 ----------------
-    B, T = 1, 2048
-    log(f"[bench] prefill B={B} T={T}: generating inputs")
-    inp = gi.make_block_inputs(2, B, T)
-    x = up(inp.x)
-    w = [up(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo)]
-    rope = torch.from_numpy(gqa.rope_table(np.arange(T))).to(dev)
-    out = torch.empty((B, T, 4096), dtype=torch.float32, device=dev)
-    ws = torch.empty(gqa.prefill_workspace_bytes(B, T), dtype=torch.uint8, device=dev)
-    step = lambda: gqa.block_forward(x, *w, rope, causal=True, out=out, workspace=ws)
-    ms, wall_ms = time_steps(step, args.steps, args.warmup)
-    F = prefill_flops(B, T)
-    value = F / (ms * 1e-3) / 1e12
-    log(f"[bench] prefill C2: {ms:.4f} ms/step (wall {wall_ms:.4f}), {value:.1f} TFLOP/s")
+    def headline(self):
+        gqa, args = self.gqa, self.args
+        B, T = 1, 2048
+        self.log(f"[bench] prefill B={B} T={T}: generating inputs")
+        inp = self.gi.make_block_inputs(2, B, T)
+        x = self.up(inp.x)
+        w = [self.up(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo)]
+        rope = self.torch.from_numpy(gqa.rope_table(np.arange(T))).to(self.dev)
+        out = self.torch.empty((B, T, 4096), dtype=self.torch.float32, device=self.dev)
+        ws = self.torch.empty(gqa.prefill_workspace_bytes(B, T), dtype=self.torch.uint8,
+                              device=self.dev)
+        step = lambda: gqa.block_forward(x, *w, rope, causal=True, out=out, workspace=ws)
+        ms, wall_ms = self.time_steps(step, args.steps, args.warmup)
+        F = prefill_flops(B, T)
+        value = F / (ms * 1e-3) / 1e12
+        self.log(f"[bench] prefill C2: {ms:.4f} ms/step (wall {wall_ms:.4f}), {value:.1f} TFLOP/s")
 
-    # per-kernel timing (stage entries launch exactly the kernels of the step)
-    q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
-    hbuf = gqa.attention(q_r, k_r, v, causal=True)
-    stages = {
-        "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
-                     lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
-        "attention": ("flash_fwd_kernel", lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf)),
-        "out_proj": ("gemm_nt_kernel (W_O GEMM, fp32 epilogue)",
-                     lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
-    }
-    sf = stage_flops(B, T)
-    kern = {}
-    for name, (kname, fn) in stages.items():
-        kms, _ = time_steps(fn, args.steps, args.warmup)
-        kern[name] = {"kernel": kname, "ms": kms, "tflops": sf[name] / (kms * 1e-3) / 1e12}
-        kern[name]["frac"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
-        log(f"[bench]   {name}: {kms:.4f} ms, {kern[name]['tflops']:.1f} TFLOP/s")
-    dom = max(kern, key=lambda k: kern[k]["ms"])
-    roofline = {"bound": "mfma", "kernel": kern[dom]["kernel"], "stage": dom,
-                "achieved": round(kern[dom]["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(kern[dom]["frac"], 4), "traffic": None,
-                "flops_per_launch": sf[dom], "avg_launch_ms": round(kern[dom]["ms"], 5)}
+        # per-kernel timing (stage entries launch exactly the kernels of the step)
+        q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
+        hbuf = gqa.attention(q_r, k_r, v, causal=True)
+        stages = {
+            "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
+                         lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
+            "attention": ("flash_fwd_kernel",
+                          lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf)),
+            "out_proj": ("gemm_nt_kernel (W_O GEMM, fp32 epilogue)",
+                         lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
+        }
+        sf = stage_flops(B, T)
+        kern = {}
+        for name, (kname, fn) in stages.items():
+            kms, _ = self.time_steps(fn, args.steps, args.warmup)
+            kern[name] = {"kernel": kname, "ms": kms, "tflops": sf[name] / (kms * 1e-3) / 1e12}
+            kern[name]["frac"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
+            self.log(f"[bench]   {name}: {kms:.4f} ms, {kern[name]['tflops']:.1f} TFLOP/s")
+        dom = max(kern, key=lambda k: kern[k]["ms"])
+        roofline = {"bound": "mfma", "kernel": kern[dom]["kernel"], "stage": dom,
+                    "achieved": round(kern[dom]["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(kern[dom]["frac"], 4), "traffic": None,
+                    "flops_per_launch": sf[dom], "avg_launch_ms": round(kern[dom]["ms"], 5)}
 
-    result = {
-        "metric": "GQA block fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "Llama-3.1-8B GQA attention block forward, prefill, causal",
-                   "B": B, "T": T, "d": 4096, "q_heads": 32, "kv_heads": 8, "d_head": 128,
-                   "rope_theta": 500000.0, "flops_per_step": F,
-                   "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
-        "roofline": roofline,
-        "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                        for kk, vv in d.items()} for k, d in kern.items()},
-    }
-    del q_r, k_r, v, hbuf
+        result = {
+            "metric": "GQA block fwd TFLOP/s (% bf16 MFMA peak) prefill; decode HBM GB/s",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "Llama-3.1-8B GQA attention block forward, prefill, causal",
+                       "B": B, "T": T, "d": 4096, "q_heads": 32, "kv_heads": 8, "d_head": 128,
+                       "rope_theta": 500000.0, "flops_per_step": F,
+                       "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+            "roofline": roofline,
+            "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                            for kk, vv in d.items()} for k, d in kern.items()},
+        }
+        return result, inp, step, out, F
 
-    # ---------------- other configurations ----------------
-    extra = {}
-    if not args.quick:
-        # decode B=64, start_pos 8191, cache 8192 rows
+    # ---------------- decode B=64, start_pos 8191, cache 8192 rows ----------------
+    def decode(self, extra):
+        torch, gqa, args = self.torch, self.gqa, self.args
         Bd, S, sp = 64, 8192, 8191
-        log("[bench] decode B=64 kv=8192: generating cache")
-        dinp = gi.make_block_inputs(4, Bd, 1, cache_len=S)
-        dx = up(dinp.x[:, 0])
-        dw = [up(a) for a in (dinp.wq, dinp.wk, dinp.wv, dinp.wo)]
-        kc, vc = up(dinp.k_cache), up(dinp.v_cache)
+        self.log("[bench] decode B=64 kv=8192: generating cache")
+        dinp = self.gi.make_block_inputs(4, Bd, 1, cache_len=S)
+        dx = self.up(dinp.x[:, 0])
+        dw = [self.up(a) for a in (dinp.wq, dinp.wk, dinp.wv, dinp.wo)]
+        kc, vc = self.up(dinp.k_cache), self.up(dinp.v_cache)
         del dinp
-        drope = torch.from_numpy(gqa.rope_table([sp])[0]).to(dev)
-        dout = torch.empty((Bd, 4096), dtype=torch.float32, device=dev)
-        dws = torch.empty(gqa.decode_workspace_bytes(Bd, S), dtype=torch.uint8, device=dev)
+        drope = torch.from_numpy(gqa.rope_table([sp])[0]).to(self.dev)
+        dout = torch.empty((Bd, 4096), dtype=torch.float32, device=self.dev)
+        dws = torch.empty(gqa.decode_workspace_bytes(Bd, S), dtype=torch.uint8, device=self.dev)
         dstep = lambda: gqa.decode_forward(dx, *dw, drope, kc, vc, sp, out=dout, workspace=dws)
-        dms, _ = time_steps(dstep, args.steps, args.warmup)
+        dms, _ = self.time_steps(dstep, args.steps, args.warmup)
         nbytes = decode_bytes(Bd, S)
-        qd = torch.zeros((Bd, 32, 128), dtype=torch.bfloat16, device=dev)
+        qd = torch.zeros((Bd, 32, 128), dtype=torch.bfloat16, device=self.dev)
         hd = torch.empty_like(qd)
-        ams, _ = time_steps(lambda: gqa.decode_attention(qd, kc, vc, S, h_out=hd, workspace=dws),
-                            args.steps, args.warmup)
+        ams, _ = self.time_steps(
+            lambda: gqa.decode_attention(qd, kc, vc, S, h_out=hd, workspace=dws),
+            args.steps, args.warmup)
         kv_bytes = Bd * S * 1024 * 2 * 2
         extra["decode_B64_kv8192"] = {
             "ms": round(dms, 5), "GB/s": round(nbytes / (dms * 1e-3) / 1e9, 1),
@@ -186,45 +173,53 @@ def main():
             "attention_kernel": {"kernel": "decode_splitkv_kernel+decode_merge_kernel",
                                  "ms": round(ams, 5),
                                  "GB/s": round(kv_bytes / (ams * 1e-3) / 1e9, 1),
-                                 "frac_of_hbm": round(kv_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}}
-        log(f"[bench] decode: {dms:.4f} ms, {extra['decode_B64_kv8192']['GB/s']} GB/s")
+                                 "frac_of_hbm": round(kv_bytes / (ams * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                      4)}}
+        self.log(f"[bench] decode: {dms:.4f} ms, {extra['decode_B64_kv8192']['GB/s']} GB/s")
         del kc, vc, dws
+        torch.cuda.empty_cache()
 
-        for (Bp, Tp, seed, steps) in ((8, 4096, 3, max(3, args.steps // 4)),
-                                      (1, 131072, 5, 2)):
-            log(f"[bench] prefill B={Bp} T={Tp}: generating inputs")
-            pinp = gi.make_block_inputs(seed, Bp, Tp)
-            px = up(pinp.x)
-            pw = [up(a) for a in (pinp.wq, pinp.wk, pinp.wv, pinp.wo)]
-            del pinp
-            prope = torch.from_numpy(gqa.rope_table(np.arange(Tp))).to(dev)
-            pout = torch.empty((Bp, Tp, 4096), dtype=torch.float32, device=dev)
-            pws = torch.empty(gqa.prefill_workspace_bytes(Bp, Tp), dtype=torch.uint8, device=dev)
-            pstep = lambda: gqa.block_forward(px, *pw, prope, causal=True, out=pout, workspace=pws)
-            pms, _ = time_steps(pstep, steps, 1)
-            Fp = prefill_flops(Bp, Tp)
-            tf = Fp / (pms * 1e-3) / 1e12
-            extra[f"prefill_B{Bp}_T{Tp}"] = {"ms": round(pms, 4), "TFLOP/s": round(tf, 1),
-                                             "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-                                             "flops_per_step": Fp, "steps": steps}
-            log(f"[bench] prefill B={Bp} T={Tp}: {pms:.3f} ms, {tf:.1f} TFLOP/s")
-            del px, pw, pout, pws
-            torch.cuda.empty_cache()
-    result["other_configs"] = extra
+    # ---------------- larger prefill configurations ----------------
+    def prefill(self, extra, Bp, Tp, seed, steps):
+        torch, gqa = self.torch, self.gqa
+        self.log(f"[bench] prefill B={Bp} T={Tp}: generating inputs")
+        pinp = self.gi.make_block_inputs(seed, Bp, Tp)
+        px = self.up(pinp.x)
+        pw = [self.up(a) for a in (pinp.wq, pinp.wk, pinp.wv, pinp.wo)]
+        del pinp
+        prope = torch.from_numpy(gqa.rope_table(np.arange(Tp))).to(self.dev)
+        pout = torch.empty((Bp, Tp, 4096), dtype=torch.float32, device=self.dev)
+        pws = torch.empty(gqa.prefill_workspace_bytes(Bp, Tp), dtype=torch.uint8, device=self.dev)
+        pstep = lambda: gqa.block_forward(px, *pw, prope, causal=True, out=pout, workspace=pws)
+        pms, _ = self.time_steps(pstep, steps, 1)
+        Fp = prefill_flops(Bp, Tp)
+        tf = Fp / (pms * 1e-3) / 1e12
+        extra[f"prefill_B{Bp}_T{Tp}"] = {"ms": round(pms, 4), "TFLOP/s": round(tf, 1),
+                                         "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                         "flops_per_step": Fp, "steps": steps}
+        self.log(f"[bench] prefill B={Bp} T={Tp}: {pms:.3f} ms, {tf:.1f} TFLOP/s")
+        del px, pw, pout, pws
+        torch.cuda.empty_cache()
+
+    def prefill_b8(self, extra):
+        self.prefill(extra, 8, 4096, 3, max(3, self.args.steps // 4))
+
+    def prefill_long(self, extra):
+        self.prefill(extra, 1, 131072, 5, 2)
 
     # ---------------- CPU oracle baseline (full headline workload) ----------------
-    if not args.no_cpu:
+    def cpu_baseline(self, result, inp, step, out, F):
         import threadpoolctl
         from oracle import gqa_oracle as O
         cores = len(os.sched_getaffinity(0))
         with threadpoolctl.threadpool_limits(cores):
             used = max([d["num_threads"] for d in threadpoolctl.threadpool_info()] or [1])
-            log(f"[bench] cpu oracle on {used} threads: B=1 T=2048 full forward")
+            self.log(f"[bench] cpu oracle on {used} threads: B=1 T=2048 full forward")
             t0 = time.perf_counter()
             ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)
             cpu_s = time.perf_counter() - t0
         step()
-        torch.cuda.synchronize()
+        self.torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.float64)
         d = ref["delta"]
         result["cpu_baseline"] = {"value": round(F / cpu_s / 1e12, 5), "unit": "TFLOP/s",
@@ -234,8 +229,57 @@ def main():
         result["parity_vs_oracle"] = {
             "relL2": float(np.linalg.norm(got - d) / np.linalg.norm(d)),
             "maxabs": float(np.max(np.abs(got - d)))}
-        log(f"[bench] cpu oracle {cpu_s:.2f} s; parity {result['parity_vs_oracle']}")
+        self.log(f"[bench] cpu oracle {cpu_s:.2f} s; parity {result['parity_vs_oracle']}")
 
+    def calibrate_copy(self, mib):
+        torch = self.torch
+        n = mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=self.dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--only", choices=["decode", "prefill_B8_T4096", "prefill_B1_T131072"],
+                    help="run just this one workload and print its figures (for profiling)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="only run a plain device copy of MB mebibytes (3 times), for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    b = Bench(args)
+    if args.calibrate_copy:
+        b.calibrate_copy(args.calibrate_copy)
+        return
+    others = {"decode": b.decode, "prefill_B8_T4096": b.prefill_b8,
+              "prefill_B1_T131072": b.prefill_long}
+    if args.only:
+        extra = {}
+        others[args.only](extra)
+        print(json.dumps({"only": args.only, **extra}), flush=True)
+        return
+
+    result, inp, step, out, F = b.headline()
+    extra = {}
+    if not args.quick:
+        for fn in others.values():
+            fn(extra)
+    result["other_configs"] = extra
+    if not args.no_cpu:
+        b.cpu_baseline(result, inp, step, out, F)
     print(json.dumps(result), flush=True)
 
 

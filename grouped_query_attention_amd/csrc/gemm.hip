@@ -21,6 +21,15 @@
 // tile, so the accumulator holds features down its rows: a lane then owns 4
 // consecutive features of one token, i.e. both members of two rotation
 // pairs, and the rotation needs no cross-lane traffic.
+//
+// Few tokens (decode, M <= 64) make both products weight streams: every
+// weight is used by at most 64 tokens, so the time is HBM bytes, and a
+// workgroup that walks all 64 K steps is bound by the latency of its own
+// step loop, with too few workgroups to keep enough bytes in flight. There
+// the reduction axis is split over SPLITK workgroups (grid y), each writing
+// fp32 partial sums to a workspace, and a second kernel adds the partials in
+// a fixed order (deterministic) and applies the epilogue (rotation + bf16,
+// or fp32 store).
 
 #include "gqa_device.h"
 #include "gqa_launch.h"
@@ -29,7 +38,7 @@ namespace gqa {
 
 constexpr int BK = 64;  // K step
 
-enum Epilogue { EPI_QKV_ROPE = 0, EPI_OUT_F32 = 1 };
+enum Epilogue { EPI_QKV_ROPE = 0, EPI_OUT_F32 = 1, EPI_PARTIAL_F32 = 2 };
 
 struct GemmArgs {
   const uint16_t* act;   // [M][4096] bf16 activations
@@ -43,8 +52,8 @@ struct GemmArgs {
   int T;                 // tokens per sequence (rope row = token % T)
   uint16_t* q_dst; long long q_bstride, q_rstride;     // elements
   uint16_t* k_dst; uint16_t* v_dst; long long kv_bstride, kv_rstride;
-  // fp32 epilogue
-  float* out;            // [M][4096]
+  // fp32 epilogue: out[M][N]; split-K partials: out + blockIdx.y*M*N
+  float* out;
 };
 
 // Chunk permutation of row r: a bijection on r & 7 for any 8 aligned rows (so 8
@@ -71,6 +80,17 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_tok, int
   int r = lin - g * per_group;
   tt = first + r % gsz;
   tf = r / gsz;
+}
+
+// Rotation of pairs (v0, v1) and (v2, v3) by the angles whose (cos, sin) are
+// (cs[0], cs[1]) and (cs[2], cs[3]) (the 2x2 rotation display of the Rotary
+// positional encoding page: first member c*z0 - s*z1, second s*z0 + c*z1).
+__device__ __forceinline__ void rotate_pairs(float& v0, float& v1, float& v2, float& v3, f32x4 cs) {
+  const float r0 = v0 * cs[0] - v1 * cs[1];
+  const float r1 = v0 * cs[1] + v1 * cs[0];
+  const float r2 = v2 * cs[2] - v3 * cs[3];
+  const float r3 = v2 * cs[3] + v3 * cs[2];
+  v0 = r0; v1 = r1; v2 = r2; v3 = r3;
 }
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
@@ -111,14 +131,19 @@ void gemm_nt_kernel(GemmArgs a) {
   const int m0 = tt * TOK;
   const int n0 = tf * FEAT;
 
+  // Fused QKV: output columns [0,4096) are W_Q rows, then W_K, then W_V.
   const uint16_t* wbase;
-  if (EPI == EPI_QKV_ROPE) {
+  if (a.N == N_QKV) {
     wbase = n0 < D_MODEL ? a.w0 + (size_t)n0 * D_MODEL
           : n0 < D_MODEL + N_KV * D_HEAD ? a.w1 + (size_t)(n0 - D_MODEL) * D_MODEL
           : a.w2 + (size_t)(n0 - D_MODEL - N_KV * D_HEAD) * D_MODEL;
   } else {
     wbase = a.w0 + (size_t)n0 * D_MODEL;
   }
+  // K range of this workgroup: all of it, or slice blockIdx.y of gridDim.y (split K)
+  constexpr int NK_ALL = D_MODEL / BK;
+  const int NK = NK_ALL / (int)gridDim.y;
+  const int k_first = (int)blockIdx.y * NK;
   const uint16_t* abase = a.act + (size_t)m0 * D_MODEL;
   const int tok_last = a.M - m0 - 1;   // rows past it are clamped (their outputs are discarded)
 
@@ -136,7 +161,7 @@ void gemm_nt_kernel(GemmArgs a) {
     const bool is_tok = C::SWAP ? !is_p : is_p;
     const int rr = is_tok ? min(r, tok_last) : r;
     const uint16_t* base = C::SWAP ? (is_p ? wbase : abase) : (is_p ? abase : wbase);
-    src[j] = base + (size_t)rr * D_MODEL + lc * 8;
+    src[j] = base + (size_t)rr * D_MODEL + (size_t)k_first * BK + lc * 8;
   }
   auto issue = [&](int kt, int stage) {
 #pragma unroll
@@ -152,9 +177,9 @@ void gemm_nt_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) acc[i][j] = f32x16{};
 
-  constexpr int NK = D_MODEL / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s, s);
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < NK) issue(s, s);
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   for (int kt = 0; kt < NK; ++kt) {
@@ -212,15 +237,8 @@ void gemm_nt_kernel(GemmArgs a) {
           const int f = n0 + wp * C::WP + i * 32 + 8 * g + 4 * lhalf - fbase;
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (region != 2) {
-            // pairs (f, f+1) and (f+2, f+3) of head f/128: pair index (f % 128)/2
-            const f32x4 cs = *reinterpret_cast<const f32x4*>(rrow + (f & (D_HEAD - 1)));
-            const float r0 = v0 * cs[0] - v1 * cs[1];
-            const float r1 = v0 * cs[1] + v1 * cs[0];
-            const float r2 = v2 * cs[2] - v3 * cs[3];
-            const float r3 = v2 * cs[3] + v3 * cs[2];
-            v0 = r0; v1 = r1; v2 = r2; v3 = r3;
-          }
+          if (region != 2)
+            rotate_pairs(v0, v1, v2, v3, *reinterpret_cast<const f32x4*>(rrow + (f & (D_HEAD - 1))));
           u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
           *reinterpret_cast<u32x2*>(drow + f) = w;
         }
@@ -228,13 +246,15 @@ void gemm_nt_kernel(GemmArgs a) {
     }
   } else {
     // acc[i][j][r]: token m0 + wp*WP + 32i + 8(r/4) + 4*lhalf + (r&3), feature n0 + wq*WQ + 32j + lrow.
+    float* obase = a.out;
+    if (EPI == EPI_PARTIAL_F32) obase += (size_t)blockIdx.y * a.M * a.N;
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = m0 + wp * C::WP + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         if (tok >= a.M) continue;
-        float* orow = a.out + (size_t)tok * D_MODEL + n0 + wq * C::WQ + lrow;
+        float* orow = obase + (size_t)tok * a.N + n0 + wq * C::WQ + lrow;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) orow[j * 32] = acc[i][j][r];
       }
@@ -242,38 +262,116 @@ void gemm_nt_kernel(GemmArgs a) {
   }
 }
 
+// Sum of the split-K partials (slices 0..ksplit-1 in order) of 4 consecutive
+// columns of one token.
+__device__ __forceinline__ f32x4 sum_partials(const GemmArgs& a, int ksplit, int tok, int col) {
+  const size_t slice = (size_t)a.M * a.N;
+  const float* p = a.out + (size_t)tok * a.N + col;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(p);
+  for (int s = 1; s < ksplit; ++s) acc += *reinterpret_cast<const f32x4*>(p + s * slice);
+  return acc;
+}
+
+// Split-K epilogue of the fused QKV product: one thread per 4 consecutive
+// columns of one token; a.out holds the partials [ksplit][M][6144].
+__global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a, int ksplit) {
+  constexpr int PER_TOK = N_QKV / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.M * PER_TOK) return;
+  const int tok = idx / PER_TOK;
+  const int col = (idx - tok * PER_TOK) * 4;
+  f32x4 v = sum_partials(a, ksplit, tok, col);
+  float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+  const int b = tok / a.T;
+  const int t = tok - b * a.T;
+  uint16_t* dst;
+  if (col < D_MODEL) {
+    dst = a.q_dst + b * a.q_bstride + t * a.q_rstride + col;
+  } else {
+    const bool is_k = col < D_MODEL + N_KV * D_HEAD;
+    const int f = col - (is_k ? D_MODEL : D_MODEL + N_KV * D_HEAD);
+    dst = (is_k ? a.k_dst : a.v_dst) + b * a.kv_bstride + t * a.kv_rstride + f;
+  }
+  if (col < D_MODEL + N_KV * D_HEAD)
+    rotate_pairs(v0, v1, v2, v3,
+                 *reinterpret_cast<const f32x4*>(a.rope + (size_t)t * (2 * 64) + (col & (D_HEAD - 1))));
+  u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+  *reinterpret_cast<u32x2*>(dst) = w;
+}
+
+// Split-K epilogue of the output projection: out[M][4096] = sum of partials.
+__global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, int ksplit, float* out) {
+  constexpr int PER_TOK = D_MODEL / 4;
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.M * PER_TOK) return;
+  const int tok = idx / PER_TOK;
+  const int col = (idx - tok * PER_TOK) * 4;
+  *reinterpret_cast<f32x4*>(out + (size_t)tok * D_MODEL + col) = sum_partials(a, ksplit, tok, col);
+}
+
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
-static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int ksplit = 1) {
   using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI>;
   const int tiles = ((a.M + TOK - 1) / TOK) * (a.N / FEAT);
-  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI>), dim3(tiles),
+  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI>), dim3(tiles, ksplit),
                      dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
 
+// Epilogue of a split-K product: a.out holds the partials [ksplit][M][N].
+static hipError_t launch_splitk_epilogue(const GemmArgs& a, int ksplit, float* final_out,
+                                         hipStream_t s) {
+  const int threads = a.M * (a.N / 4);
+  const dim3 grid((threads + 255) / 256);
+  if (a.N == N_QKV)
+    hipLaunchKernelGGL(splitk_qkv_rope_kernel, grid, dim3(256), 0, s, a, ksplit);
+  else
+    hipLaunchKernelGGL(splitk_out_kernel, grid, dim3(256), 0, s, a, ksplit, final_out);
+  return hipGetLastError();
+}
+
+// Split-K product into the partial buffer `part` ([ksplit][M][N] fp32), then
+// the epilogue kernel. a.out is the final fp32 destination (out_proj) or unused.
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES>
+static hipError_t launch_gemm_splitk(GemmArgs a, float* part, int ksplit, hipStream_t s) {
+  float* final_out = a.out;
+  a.out = part;
+  hipError_t e = launch_gemm<TOK, FEAT, WPN, WQN, STAGES, EPI_PARTIAL_F32>(a, s, ksplit);
+  if (e != hipSuccess) return e;
+  return launch_splitk_epilogue(a, ksplit, final_out, s);
+}
+
 #ifndef GQA_GEMM_NO_LAUNCHERS
+constexpr int SPLITK_MAX_M = 64;
+constexpr int SPLITK = 4;
+
+size_t gemm_splitk_bytes(int M) {
+  return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * N_QKV * sizeof(float) : 0;
+}
+
 hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
-                           long long kv_rstride, hipStream_t s) {
+                           long long kv_rstride, float* splitk, hipStream_t s) {
   GemmArgs a{};
   a.act = x; a.w0 = wq; a.w1 = wk; a.w2 = wv; a.M = M; a.N = N_QKV;
   a.rope = rope; a.T = T;
   a.q_dst = q_dst; a.q_bstride = q_bstride; a.q_rstride = q_rstride;
   a.k_dst = k_dst; a.v_dst = v_dst; a.kv_bstride = kv_bstride; a.kv_rstride = kv_rstride;
-  // Few tokens (decode): thin weight strips and a deep load ring, so the weights
-  // stream from HBM through many workgroups; otherwise the largest tile that
-  // still fills the chip.
+  // Few tokens (decode): split K with a workspace, else thin weight strips and a
+  // deep load ring; otherwise the largest tile that still fills the chip.
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4>(a, splitk, SPLITK, s);
   if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);
   return launch_gemm<256, 256, 4, 2, 2, EPI_QKV_ROPE>(a, s);
 }
 
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
-                           hipStream_t s) {
+                           float* splitk, hipStream_t s) {
   GemmArgs a{};
   a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1;
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4>(a, splitk, SPLITK, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
   return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);

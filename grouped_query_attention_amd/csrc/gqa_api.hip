@@ -21,8 +21,10 @@ constexpr size_t KV_W = (size_t)N_KV * D_HEAD;  // 1024 features of K or V per t
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
+// Prefill: Q_r, K_r, V, H (bf16), then the projections' split-reduction
+// scratch (only for M <= 64 tokens).
 struct PrefillWs {
-  size_t q, k, v, h, total;
+  size_t q, k, v, h, splitk, total;
 };
 
 inline PrefillWs prefill_layout(long long M) {
@@ -32,10 +34,13 @@ inline PrefillWs prefill_layout(long long M) {
   w.k = w.q + align_up(m * D_MODEL * 2);
   w.v = w.k + align_up(m * KV_W * 2);
   w.h = w.v + align_up(m * KV_W * 2);
-  w.total = w.h + align_up(m * D_MODEL * 2);
+  w.splitk = w.h + align_up(m * D_MODEL * 2);
+  w.total = w.splitk + align_up(gqa::gemm_splitk_bytes((int)M));   // M <= GQA_MAX_TOKENS
   return w;
 }
 
+// Decode: Q_r, H (bf16), then one fp32 region shared, one kernel at a time, by
+// the projections' split-reduction partials and the attention's split-KV partials.
 struct DecodeWs {
   size_t q, h, part, total;
 };
@@ -45,7 +50,9 @@ inline DecodeWs decode_layout(int B, int S_max) {
   w.q = 0;
   w.h = align_up((size_t)B * D_MODEL * 2);
   w.part = w.h + align_up((size_t)B * D_MODEL * 2);
-  w.total = w.part + align_up(gqa::decode_partials_bytes(B, S_max));
+  const size_t attn = gqa::decode_partials_bytes(B, S_max);
+  const size_t proj = gqa::gemm_splitk_bytes(B);
+  w.total = w.part + align_up(attn > proj ? attn : proj);
   return w;
 }
 
@@ -126,7 +133,8 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
   const long long M = (long long)B * T;
   return hip_status(gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q_r,
                                          (long long)T * D_MODEL, D_MODEL, k_r, v,
-                                         (long long)T * KV_W, KV_W, (hipStream_t)stream));
+                                         (long long)T * KV_W, KV_W, nullptr,
+                                         (hipStream_t)stream));
 }
 
 int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
@@ -150,7 +158,7 @@ int gqa_output_projection(const gqa_bf16* h, const gqa_bf16* w_o, int M, float* 
   if (!h || !w_o || !out) return GQA_ERR_NULL;
   if (M < 1 || M > GQA_MAX_TOKENS) return GQA_ERR_SHAPE;
   if (misaligned(h) || misaligned(w_o) || misaligned(out)) return GQA_ERR_ALIGN;
-  return hip_status(gqa::launch_out_proj(h, w_o, M, out, (hipStream_t)stream));
+  return hip_status(gqa::launch_out_proj(h, w_o, M, out, nullptr, (hipStream_t)stream));
 }
 
 int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
@@ -178,16 +186,17 @@ int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_
   auto* k = reinterpret_cast<gqa_bf16*>(ws + L.k);
   auto* v = reinterpret_cast<gqa_bf16*>(ws + L.v);
   gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* splitk = L.total > L.splitk ? reinterpret_cast<float*>(ws + L.splitk) : nullptr;
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
                                       (long long)T * D_MODEL, D_MODEL, k, v,
-                                      (long long)T * KV_W, KV_W, s);
+                                      (long long)T * KV_W, KV_W, splitk, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
                                   h, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, s));
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, splitk, s));
 }
 
 int gqa_decode_attention(const gqa_bf16* q_r, const gqa_bf16* k_cache,
@@ -233,11 +242,12 @@ int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w
 
   hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, B, 1, q, D_MODEL, 0,
                                       k_cache + (size_t)start_pos * KV_W,
-                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, 0, s);
+                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, 0,
+                                      part, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, B, out, s));
+  return hip_status(gqa::launch_out_proj(h, w_o, B, out, part, s));
 }
 
 }  // extern "C"

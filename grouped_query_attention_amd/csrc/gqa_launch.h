@@ -11,15 +11,20 @@ namespace gqa {
 // rope row = token % T). Destination of token m = b*T + t:
 //   Q row: q_dst + b*q_bstride + t*q_rstride           (4096 elements)
 //   K/V row: k_dst/v_dst + b*kv_bstride + t*kv_rstride  (1024 elements)
+// `splitk` (may be null) is fp32 scratch of gemm_splitk_bytes(M) bytes: with
+// it, M <= 64 products split the reduction across workgroups (decode).
 hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
-                           long long kv_rstride, hipStream_t s);
+                           long long kv_rstride, float* splitk, hipStream_t s);
 
-// out[M][4096] (fp32) = h[M][4096] · w_oᵀ
+// out[M][4096] (fp32) = h[M][4096] · w_oᵀ; `splitk` as for launch_qkv_rope.
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
-                           hipStream_t s);
+                           float* splitk, hipStream_t s);
+
+// Scratch bytes of the split-reduction path for M tokens (0 when M > 64).
+size_t gemm_splitk_bytes(int M);
 
 // Prefill grouped flash attention. q_r/h_out [B][T][32][128]; k/v rows of
 // sequence b start at k + b*kv_bstride (row stride 1024 elements); query i is

@@ -113,7 +113,9 @@ def test_attention_explicit_mask():
 
 # --- whole block ---------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,T,seed", [(1, 128, 1), (2, 77, 21), (3, 129, 22), (1, 1, 23)])
+# (2, 30): 60 tokens take the projections' split-reduction path (M <= 64)
+@pytest.mark.parametrize("B,T,seed", [(1, 128, 1), (2, 77, 21), (3, 129, 22), (1, 1, 23),
+                                      (2, 30, 24)])
 def test_block_forward_small(B, T, seed):
     print(f"[case] block_forward B={B} T={T} seed={seed}", flush=True)
     inp = gi.make_block_inputs(seed, B, T)
