@@ -107,12 +107,16 @@ class Bench:
 
         # per-kernel timing (stage entries launch exactly the kernels of the step)
         q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
-        hbuf = gqa.attention(q_r, k_r, v, causal=True)
+        aws_n = gqa.attention_workspace_bytes(B, T, T, True)
+        aws = self.torch.empty(max(aws_n, 1), dtype=self.torch.uint8, device=self.dev)
+        hbuf = gqa.attention(q_r, k_r, v, causal=True, workspace=aws if aws_n else None)
         stages = {
             "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
                          lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
-            "attention": ("flash_fwd_kernel",
-                          lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf)),
+            "attention": ("flash_fwd_kernel + flash_merge_kernel (balanced causal launch)"
+                          if aws_n else "flash_fwd_kernel",
+                          lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf,
+                                                workspace=aws if aws_n else None)),
             "out_proj": ("gemm_nt_kernel (W_O GEMM, fp32 epilogue)",
                          lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
         }

@@ -52,10 +52,11 @@ def _load():
         "gqa_rope_table": (I, [P, I, D, P]),
         "gqa_prefill_workspace_bytes": (Z, [I, I]),
         "gqa_decode_workspace_bytes": (Z, [I, I]),
+        "gqa_attention_workspace_bytes": (Z, [I, I, I, I]),
         "gqa_block_forward": (I, [P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_decode_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P, Z, P]),
         "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, P]),
-        "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P]),
+        "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P, Z, P]),
         "gqa_output_projection": (I, [P, P, I, P, P]),
         "gqa_decode_attention": (I, [P, P, P, I, I, I, P, P, Z, P]),
     }
@@ -74,7 +75,8 @@ def lib():
 
 def exported_symbols():
     return ["gqa_status_string", "gqa_dims", "gqa_rope_table", "gqa_prefill_workspace_bytes",
-            "gqa_decode_workspace_bytes", "gqa_block_forward", "gqa_decode_forward",
+            "gqa_decode_workspace_bytes", "gqa_attention_workspace_bytes",
+            "gqa_block_forward", "gqa_decode_forward",
             "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention"]
 
 
@@ -135,6 +137,10 @@ def prefill_workspace_bytes(B: int, T: int) -> int:
 
 def decode_workspace_bytes(B: int, S_max: int) -> int:
     return int(_load().gqa_decode_workspace_bytes(B, S_max))
+
+
+def attention_workspace_bytes(B: int, T: int, kv_len: int, causal: bool = True) -> int:
+    return int(_load().gqa_attention_workspace_bytes(B, T, kv_len, int(bool(causal))))
 
 
 # --- device entries -------------------------------------------------------------------
@@ -208,15 +214,26 @@ def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None)
     return q_r, k_r, v
 
 
-def attention(q_r, k_r, v, *, causal: bool = True, mask=None, h_out=None, stream=None):
-    """H [B,T,32,128] bf16 from rotated queries/keys and values."""
+def attention(q_r, k_r, v, *, causal: bool = True, mask=None, h_out=None, workspace=None,
+              balanced: bool = True, stream=None):
+    """H [B,T,32,128] bf16 from rotated queries/keys and values. With `balanced`
+    (default) a causal launch of few query tiles gets its workspace (allocated
+    here unless given); balanced=False runs the plain launch."""
     import torch
     B, T = q_r.shape[:2]
     kv_len = k_r.shape[1]
     if h_out is None:
         h_out = torch.empty((B, T, N_HEADS, D_HEAD), dtype=torch.bfloat16, device=q_r.device)
+    if balanced and workspace is None:
+        nb = attention_workspace_bytes(B, T, kv_len, causal)
+        if nb:
+            workspace = torch.empty(nb, dtype=torch.uint8, device=q_r.device)
+    if not balanced:
+        workspace = None
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().gqa_attention(_ptr(q_r), _ptr(k_r), _ptr(v), _ptr(mask), int(bool(causal)),
-                               B, T, kv_len, _ptr(h_out), _stream(stream))
+                               B, T, kv_len, _ptr(h_out), _ptr(workspace), wsb,
+                               _stream(stream))
     _check("gqa_attention", st)
     return h_out
 

@@ -73,27 +73,59 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Causal work balance. With few query tiles (B * 8 * tiles under two per CU),
+// the longest workgroup (the last query tile attends to every key tile) sets
+// the time: at T = 2048 it does 32 key tiles while the mean is 16.5. Such
+// launches are planned on the host, stream-K style: per (sequence, KV head)
+// the query tiles are laid out in the order last, first, second-to-last,
+// second, ... (so a long tile is followed by a short one), their key tiles are
+// concatenated, and the stream is cut into equal bins; workgroup (bin, b, g)
+// runs the pieces of its bin one after the other. A query tile cut across two
+// bins is computed in pieces; a piece writes an unnormalised fp32 partial
+// (O, running max, running sum) per query row, and flash_merge_kernel
+// combines the pieces of each cut tile, exactly as the online softmax
+// combines key tiles.
+constexpr int FA_MAX_ENT = 256;    // (query tile, key range) entries of a plan
+constexpr int FA_MAX_BINS = 256;   // bins per (sequence, KV head)
+constexpr int FA_MAX_MERGE = 128;  // cut query tiles of a plan
+constexpr int FA_PLAN_CUS = 256;   // CUs the plan balances over (MI355X)
+constexpr int FA_MIN_PIECE = 4;    // key tiles: bins never hold fewer
+constexpr int FA_DIRECT = 255;     // slot value of an entry that writes H itself
+// Partial of one piece for one (sequence, KV head): O[4 heads][64 rows][128],
+// then max[4][64], then sum[4][64], fp32.
+constexpr int FA_PART = N_REP * FA_BQ * D_HEAD + 2 * N_REP * FA_BQ;
+constexpr int FA_MERGE_ROWS = 8;   // (head, query) rows per merge workgroup
+
 struct FlashArgs {
   const uint16_t* q; const uint16_t* k; const uint16_t* v;
   long long kv_bstride;
   const float* mask;     // [T][kv_len] or null
   uint16_t* h;
+  float* part;           // piece partials [slot][B][8][FA_PART] (planned launches)
   int B, T, kv_len, q_pos0, causal, n_qtiles;
+  // planned launch: workgroup i runs bin i / (8B) for (b, g) = split of i % (8B),
+  // i.e. entries bin_start[bin] .. bin_start[bin + 1] - 1, each
+  // qtile | first key tile << 8 | end key tile << 16 | slot << 24
+  int n_bins;
+  unsigned short bin_start[FA_MAX_BINS + 1];
+  unsigned ent[FA_MAX_ENT];
 };
 
-__global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[FA_STAGES * 2 * FA_TILE];
+struct FlashMergeArgs {
+  float* part; uint16_t* h;
+  int B, T;
+  unsigned mrg[FA_MAX_MERGE];   // qtile | first slot << 8 | pieces << 16
+};
 
+// One (query tile, key tiles kt0..kt1-1) entry for (sequence b, KV head g).
+__device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, int b, int g,
+                                            int qt, int kt0, int kt1, int slot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
   // Waves w and w+4 share a SIMD. The first four run each tile as QK -> softmax
   // -> P·V; the other four run the P·V of the previous tile first, so on every
   // SIMD one wave's MFMAs overlap the other's softmax between two barriers.
   const bool lag = wave >= 4;
-  const int g = blockIdx.x & (N_KV - 1);
-  const int rest = blockIdx.x >> 3;
-  const int b = rest % a.B;
-  const int qt = a.causal ? (a.n_qtiles - 1 - rest / a.B) : (rest / a.B);
   const int q0 = qt * FA_BQ;
   const int h = g * N_REP + (wave & 3);
   const int qi = q0 + (wave >> 2) * 32 + lrow;        // this lane's query index
@@ -104,9 +136,6 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
 
   u32x4 qf[8];
 
-  int kv_end = a.kv_len;
-  if (a.causal) kv_end = min(kv_end, a.q_pos0 + q0 + FA_BQ);
-  const int n_tiles = (kv_end + FA_BN - 1) / FA_BN;
 
   // Direct-to-LDS loads of tile t: instruction i (0..31) covers rows 4(i&15)..+3
   // of K (i < 16) or V; lane l writes row 4(i&15) + (l >> 4), physical chunk
@@ -222,8 +251,8 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
       }
   };
 
-  issue(0);
-  if (n_tiles > 1) issue(1);
+  issue(kt0);
+  if (kt0 + 1 < kt1) issue(kt0 + 1);
   // Query fragments (MFMA B operand): k-step s covers d = 16s + 8*lhalf .. +7.
   {
     const bool ok = qi < a.T;
@@ -241,21 +270,39 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   wait_vmcnt<0>();
   // trip t: tile t is computed (the lagging waves finish tile t-1); one extra
   // trip lets the lagging waves do the last P·V.
-  for (int t = 0; t <= n_tiles; ++t) {
+  for (int t = kt0; t <= kt1; ++t) {
     // tile t resident (tile t+1 may still be in flight); every wave is past
     // trip t-1, so stage (t+2)%4 — last read as tile t-2 — is free
-    if (t + 1 < n_tiles) wait_vmcnt<FA_NI_W>(); else wait_vmcnt<0>();
+    if (t + 1 < kt1) wait_vmcnt<FA_NI_W>(); else wait_vmcnt<0>();
     barrier_no_fence();
-    if (t + 2 < n_tiles) issue(t + 2);
+    if (t + 2 < kt1) issue(t + 2);
     if (!lag) {
-      if (t < n_tiles) { qk_softmax(t); pv(t); }
+      if (t < kt1) { qk_softmax(t); pv(t); }
     } else {
-      if (t > 0) pv(t - 1);
-      if (t < n_tiles) qk_softmax(t);
+      if (t > kt0) pv(t - 1);
+      if (t < kt1) qk_softmax(t);
     }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (slot != FA_DIRECT) {
+    // piece of a cut query tile: unnormalised partial, rows beyond T included
+    // (the merge skips them)
+    float* pp = a.part + ((size_t)(slot * a.B + b) * N_KV + g) * FA_PART;
+    const int row = (wave & 3) * FA_BQ + (wave >> 2) * 32 + lrow;   // head h4, query qi - q0
+    float* orow = pp + (size_t)row * D_HEAD + 4 * lhalf;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *reinterpret_cast<f32x4*>(orow + db * 32 + gq * 8) =
+            f32x4{o[db][4 * gq], o[db][4 * gq + 1], o[db][4 * gq + 2], o[db][4 * gq + 3]};
+    if (lhalf == 0) {
+      pp[N_REP * FA_BQ * D_HEAD + row] = m_ref;
+      pp[N_REP * FA_BQ * D_HEAD + N_REP * FA_BQ + row] = l_tot;
+    }
+    return;
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qi < a.T) {
     uint16_t* hrow = a.h + ((size_t)(b * a.T + qi) * N_HEADS + h) * D_HEAD + 4 * lhalf;
@@ -270,16 +317,201 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   }
 }
 
+__global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[FA_STAGES * 2 * FA_TILE];
+  const int g = blockIdx.x & (N_KV - 1);
+  const int rest = blockIdx.x >> 3;
+  const int b = rest % a.B;
+  if (a.n_bins > 0) {
+    const int bin = rest / a.B;
+    const int e1 = a.bin_start[bin + 1];
+    for (int i = a.bin_start[bin]; i < e1; ++i) {
+      const unsigned e = a.ent[i];
+      // every wave is done with the LDS ring of the previous entry
+      if (i > a.bin_start[bin]) barrier_no_fence();
+      flash_entry(a, smem, b, g, e & 255, (e >> 8) & 255, (e >> 16) & 255, e >> 24);
+    }
+    return;
+  }
+  // plain launch: one query tile per workgroup, longest first when causal
+  const int qt = a.causal ? (a.n_qtiles - 1 - rest / a.B) : (rest / a.B);
+  int kv_end = a.kv_len;
+  if (a.causal) kv_end = min(kv_end, a.q_pos0 + (qt + 1) * FA_BQ);
+  flash_entry(a, smem, b, g, qt, 0, (kv_end + FA_BN - 1) / FA_BN, FA_DIRECT);
+}
+
+// Combines the pieces of cut query tiles. Workgroup (r, t, b, g) takes rows
+// 8r .. 8r+7 of (head, query) of cut tile t; each 32-lane half-wave takes one
+// row, lane i holding d = 4i .. 4i+3. Pieces are rescaled to their common max
+// and summed, then divided by the summed row sums (pieces in slot order).
+__global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
+  constexpr int MAXP = 4;
+  const int g = blockIdx.x & (N_KV - 1);
+  int rest = blockIdx.x >> 3;
+  const int b = rest % a.B;
+  rest /= a.B;
+  const int rblk = rest % (N_REP * FA_BQ / FA_MERGE_ROWS);
+  const unsigned e = a.mrg[rest / (N_REP * FA_BQ / FA_MERGE_ROWS)];
+  const int qt = e & 255, slot0 = (e >> 8) & 255, np = (e >> 16) & 255;
+  const int li = threadIdx.x & 31;
+  const int row = rblk * FA_MERGE_ROWS + (threadIdx.x >> 5);
+  const int h4 = row / FA_BQ, qi = qt * FA_BQ + row % FA_BQ;
+  if (qi >= a.T) return;
+  const size_t piece_stride = (size_t)a.B * N_KV * FA_PART;
+  const float* base = a.part + ((size_t)(slot0 * a.B + b) * N_KV + g) * FA_PART;
+  float mp[MAXP], lp[MAXP];
+  f32x4 op[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (p < np) {
+      const float* pp = base + p * piece_stride;
+      mp[p] = pp[N_REP * FA_BQ * D_HEAD + row];
+      lp[p] = pp[N_REP * FA_BQ * D_HEAD + N_REP * FA_BQ + row];
+      op[p] = *reinterpret_cast<const f32x4*>(pp + (size_t)row * D_HEAD + 4 * li);
+    } else {
+      mp[p] = NEG_INF; lp[p] = 0.f; op[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  float M = mp[0];
+#pragma unroll
+  for (int p = 1; p < MAXP; ++p) M = fmaxf(M, mp[p]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const float f = mp[p] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((mp[p] - M) * SCALE_LOG2);
+    acc += op[p] * f;
+    L += lp[p] * f;
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const int h = g * N_REP + h4;
+  uint16_t* hrow = a.h + ((size_t)(b * a.T + qi) * N_HEADS + h) * D_HEAD + 4 * li;
+  *reinterpret_cast<u32x2*>(hrow) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                          pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+}
+
+namespace {
+
+constexpr int FA_MERGE_MAXP = 4;   // pieces per cut query tile (flash_merge_kernel)
+
+struct FlashPlan {
+  int n_bins = 0, n_ent = 0, n_merge = 0, n_slots = 0;
+  unsigned short bin_start[FA_MAX_BINS + 1];
+  unsigned ent[FA_MAX_ENT];
+  unsigned mrg[FA_MAX_MERGE];
+};
+
+// Key tiles of query tile qt (causal).
+inline int flash_key_tiles(int qt, int kv_len, int q_pos0) {
+  const int kv_end = min(kv_len, q_pos0 + (qt + 1) * FA_BQ);
+  return (kv_end + FA_BN - 1) / FA_BN;
+}
+
+// Plans a causal launch with too few query tiles to balance; returns false
+// (plain launch) when no plan applies or it would not fit its tables.
+bool flash_plan(int B, int T, int kv_len, int q_pos0, int causal, FlashPlan& p) {
+  p = FlashPlan{};
+  if (!causal) return false;
+  const int nq = (T + FA_BQ - 1) / FA_BQ;
+  if ((long long)B * N_KV * nq >= 2LL * FA_PLAN_CUS || nq > 255) return false;
+  // zigzag order of query tiles and the unit (key tile) stream per (b, g)
+  int order[256], len[256];
+  long long U = 0;
+  int longest = 0;
+  for (int i = 0; i < nq; ++i) {
+    order[i] = (i & 1) ? i / 2 : nq - 1 - i / 2;
+    len[i] = flash_key_tiles(order[i], kv_len, q_pos0);
+    U += len[i];
+    longest = max(longest, len[i]);
+  }
+  if (longest > 255) return false;
+  int bins = FA_PLAN_CUS / (B * N_KV);
+  if ((long long)bins > U / FA_MIN_PIECE) bins = (int)(U / FA_MIN_PIECE);
+  bins = min(bins, FA_MAX_BINS);
+  if (bins < 2) return false;
+  // worth it only when the longest tile clearly exceeds a bin
+  if (2 * (long long)longest * bins < 3 * U) return false;
+  // bin s holds stream units [U*s/bins, U*(s+1)/bins)
+  auto cut = [&](int s) { return (int)(U * s / bins); };
+  // pass 1: pieces per query tile; pass 2: entries, slots, merges
+  int pieces_of[256];
+  for (int pass = 0; pass < 2; ++pass) {
+    int pos = 0, qi = 0, kt = 0;   // stream position; current query tile (order index), key tile
+    int next_slot[256];
+    if (pass == 1) {
+      p.n_slots = 0;
+      for (int i = 0; i < nq; ++i) {
+        next_slot[i] = FA_DIRECT;
+        if (pieces_of[i] > 1) {
+          if (pieces_of[i] > FA_MERGE_MAXP || p.n_merge >= FA_MAX_MERGE) return false;
+          next_slot[i] = p.n_slots;
+          p.mrg[p.n_merge++] = (unsigned)order[i] | (unsigned)p.n_slots << 8 |
+                               (unsigned)pieces_of[i] << 16;
+          p.n_slots += pieces_of[i];
+        }
+      }
+      if (p.n_slots >= FA_DIRECT) return false;
+    } else {
+      for (int i = 0; i < nq; ++i) pieces_of[i] = 0;
+    }
+    for (int s = 0; s < bins; ++s) {
+      if (pass == 1) p.bin_start[s] = (unsigned short)p.n_ent;
+      const int end = cut(s + 1);
+      while (pos < end) {
+        const int take = min(end - pos, len[qi] - kt);
+        if (pass == 0) {
+          ++pieces_of[qi];
+        } else {
+          if (p.n_ent >= FA_MAX_ENT) return false;
+          const int slot = next_slot[qi] == FA_DIRECT ? FA_DIRECT : next_slot[qi]++;
+          p.ent[p.n_ent++] = (unsigned)order[qi] | (unsigned)kt << 8 |
+                             (unsigned)(kt + take) << 16 | (unsigned)slot << 24;
+        }
+        pos += take;
+        kt += take;
+        if (kt == len[qi]) { ++qi; kt = 0; }
+      }
+    }
+    if (pass == 1) p.bin_start[bins] = (unsigned short)p.n_ent;
+  }
+  p.n_bins = bins;
+  return true;
+}
+
+}  // namespace
+
+size_t flash_partials_bytes(int B, int T, int kv_len, int causal) {
+  FlashPlan p;
+  if (!flash_plan(B, T, kv_len, 0, causal, p)) return 0;
+  return (size_t)p.n_slots * B * N_KV * FA_PART * sizeof(float);
+}
+
 hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
                                   long long kv_bstride, const float* mask, int causal, int B,
                                   int T, int kv_len, int q_pos0, uint16_t* h_out,
-                                  hipStream_t s) {
+                                  float* partials, hipStream_t s) {
   FlashArgs a{};
   a.q = q_r; a.k = k; a.v = v; a.kv_bstride = kv_bstride; a.mask = mask; a.h = h_out;
   a.B = B; a.T = T; a.kv_len = kv_len; a.q_pos0 = q_pos0; a.causal = causal;
   a.n_qtiles = (T + FA_BQ - 1) / FA_BQ;
-  const long long grid = (long long)a.n_qtiles * B * N_KV;
+  FlashPlan plan;
+  const bool planned = partials && flash_plan(B, T, kv_len, q_pos0, causal, plan);
+  long long grid = (long long)a.n_qtiles * B * N_KV;
+  if (planned) {
+    a.part = partials;
+    a.n_bins = plan.n_bins;
+    for (int i = 0; i <= plan.n_bins; ++i) a.bin_start[i] = plan.bin_start[i];
+    for (int i = 0; i < plan.n_ent; ++i) a.ent[i] = plan.ent[i];
+    grid = (long long)plan.n_bins * B * N_KV;
+  }
   hipLaunchKernelGGL(flash_fwd_kernel, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !planned || plan.n_merge == 0) return e;
+  FlashMergeArgs m{};
+  m.part = partials; m.h = h_out; m.B = B; m.T = T;
+  for (int i = 0; i < plan.n_merge; ++i) m.mrg[i] = plan.mrg[i];
+  const long long mgrid = (long long)plan.n_merge * B * N_KV * (N_REP * FA_BQ / FA_MERGE_ROWS);
+  hipLaunchKernelGGL(flash_merge_kernel, dim3((unsigned)mgrid), dim3(256), 0, s, m);
   return hipGetLastError();
 }
 
@@ -490,9 +722,12 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
   const int g = h / N_REP, q = h % N_REP;
   const int d = threadIdx.x;
   const float* base = a.part + (size_t)(b * N_KV + g) * a.n_split * DC_PART;
+  // unrolled so that several splits' loads are in flight at once
   float M = NEG_INF;
+#pragma unroll 8
   for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * DC_PART + N_REP * D_HEAD + q]);
   float acc = 0.f, L = 0.f;
+#pragma unroll 8
   for (int s = 0; s < a.n_split; ++s) {
     const float* p = base + s * DC_PART;
     const float ms = p[N_REP * D_HEAD + q];

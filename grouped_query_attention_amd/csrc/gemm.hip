@@ -93,6 +93,16 @@ __device__ __forceinline__ void rotate_pairs(float& v0, float& v1, float& v2, fl
   v0 = r0; v1 = r1; v2 = r2; v3 = r3;
 }
 
+// Row f of the weight operand: for the fused QKV product (N = 6144), output
+// columns [0,4096) are W_Q rows, then W_K, then W_V; otherwise W_O rows.
+__device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int f) {
+  if (a.N == N_QKV) {
+    if (f >= D_MODEL + N_KV * D_HEAD) return a.w2 + (size_t)(f - D_MODEL - N_KV * D_HEAD) * D_MODEL;
+    if (f >= D_MODEL) return a.w1 + (size_t)(f - D_MODEL) * D_MODEL;
+  }
+  return a.w0 + (size_t)f * D_MODEL;
+}
+
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
 struct GemmCfg {
   static constexpr bool SWAP = (EPI == EPI_QKV_ROPE);
@@ -131,15 +141,6 @@ void gemm_nt_kernel(GemmArgs a) {
   const int m0 = tt * TOK;
   const int n0 = tf * FEAT;
 
-  // Fused QKV: output columns [0,4096) are W_Q rows, then W_K, then W_V.
-  const uint16_t* wbase;
-  if (a.N == N_QKV) {
-    wbase = n0 < D_MODEL ? a.w0 + (size_t)n0 * D_MODEL
-          : n0 < D_MODEL + N_KV * D_HEAD ? a.w1 + (size_t)(n0 - D_MODEL) * D_MODEL
-          : a.w2 + (size_t)(n0 - D_MODEL - N_KV * D_HEAD) * D_MODEL;
-  } else {
-    wbase = a.w0 + (size_t)n0 * D_MODEL;
-  }
   // K range of this workgroup: all of it, or slice blockIdx.y of gridDim.y (split K)
   constexpr int NK_ALL = D_MODEL / BK;
   const int NK = NK_ALL / (int)gridDim.y;
@@ -159,9 +160,9 @@ void gemm_nt_kernel(GemmArgs a) {
     const bool is_p = row < PR;
     const int r = is_p ? row : row - PR;
     const bool is_tok = C::SWAP ? !is_p : is_p;
-    const int rr = is_tok ? min(r, tok_last) : r;
-    const uint16_t* base = C::SWAP ? (is_p ? wbase : abase) : (is_p ? abase : wbase);
-    src[j] = base + (size_t)rr * D_MODEL + (size_t)k_first * BK + lc * 8;
+    const uint16_t* rowp = is_tok ? abase + (size_t)min(r, tok_last) * D_MODEL
+                                  : weight_row(a, n0 + r);
+    src[j] = rowp + (size_t)k_first * BK + lc * 8;
   }
   auto issue = [&](int kt, int stage) {
 #pragma unroll
@@ -218,23 +219,25 @@ void gemm_nt_kernel(GemmArgs a) {
 
   if (EPI == EPI_QKV_ROPE) {
     // acc[i][j][4g + e]: feature n0 + wp*WP + 32i + 8g + 4*lhalf + e, token m0 + wq*WQ + 32j + lrow.
-    const int region = n0 < D_MODEL ? 0 : (n0 < D_MODEL + N_KV * D_HEAD ? 1 : 2);
-    const int fbase = region == 0 ? 0 : (region == 1 ? D_MODEL : D_MODEL + N_KV * D_HEAD);
+    // A 32-feature block lies inside one of Q, K, V (their bounds are multiples of 1024).
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const int tok = m0 + wq * C::WQ + j * 32 + lrow;
       if (tok >= a.M) continue;
       const int b = tok / a.T;
       const int t = tok - b * a.T;
-      uint16_t* drow;
-      if (region == 0) drow = a.q_dst + b * a.q_bstride + t * a.q_rstride;
-      else drow = (region == 1 ? a.k_dst : a.v_dst) + b * a.kv_bstride + t * a.kv_rstride;
       const float* rrow = a.rope + (size_t)t * (2 * 64);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
+        const int fblk = n0 + wp * C::WP + i * 32;
+        const int region = fblk < D_MODEL ? 0 : (fblk < D_MODEL + N_KV * D_HEAD ? 1 : 2);
+        const int fbase = region == 0 ? 0 : (region == 1 ? D_MODEL : D_MODEL + N_KV * D_HEAD);
+        uint16_t* drow;
+        if (region == 0) drow = a.q_dst + b * a.q_bstride + t * a.q_rstride;
+        else drow = (region == 1 ? a.k_dst : a.v_dst) + b * a.kv_bstride + t * a.kv_rstride;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = n0 + wp * C::WP + i * 32 + 8 * g + 4 * lhalf - fbase;
+          const int f = fblk + 8 * g + 4 * lhalf - fbase;
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
           if (region != 2)
@@ -262,25 +265,31 @@ void gemm_nt_kernel(GemmArgs a) {
   }
 }
 
-// Sum of the split-K partials (slices 0..ksplit-1 in order) of 4 consecutive
-// columns of one token.
-__device__ __forceinline__ f32x4 sum_partials(const GemmArgs& a, int ksplit, int tok, int col) {
+// Sum of the split-K partials (slices 0..KS-1 in order) of 4 consecutive
+// columns of one token; all KS loads are issued before the adds.
+template <int KS>
+__device__ __forceinline__ f32x4 sum_partials(const GemmArgs& a, int tok, int col) {
   const size_t slice = (size_t)a.M * a.N;
   const float* p = a.out + (size_t)tok * a.N + col;
-  f32x4 acc = *reinterpret_cast<const f32x4*>(p);
-  for (int s = 1; s < ksplit; ++s) acc += *reinterpret_cast<const f32x4*>(p + s * slice);
+  f32x4 v[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) v[s] = *reinterpret_cast<const f32x4*>(p + s * slice);
+  f32x4 acc = v[0];
+#pragma unroll
+  for (int s = 1; s < KS; ++s) acc += v[s];
   return acc;
 }
 
 // Split-K epilogue of the fused QKV product: one thread per 4 consecutive
-// columns of one token; a.out holds the partials [ksplit][M][6144].
-__global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a, int ksplit) {
+// columns of one token; a.out holds the partials [KS][M][6144].
+template <int KS>
+__global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a) {
   constexpr int PER_TOK = N_QKV / 4;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.M * PER_TOK) return;
   const int tok = idx / PER_TOK;
   const int col = (idx - tok * PER_TOK) * 4;
-  f32x4 v = sum_partials(a, ksplit, tok, col);
+  f32x4 v = sum_partials<KS>(a, tok, col);
   float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
   const int b = tok / a.T;
   const int t = tok - b * a.T;
@@ -300,13 +309,14 @@ __global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a, int ks
 }
 
 // Split-K epilogue of the output projection: out[M][4096] = sum of partials.
-__global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, int ksplit, float* out) {
+template <int KS>
+__global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, float* out) {
   constexpr int PER_TOK = D_MODEL / 4;
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.M * PER_TOK) return;
   const int tok = idx / PER_TOK;
   const int col = (idx - tok * PER_TOK) * 4;
-  *reinterpret_cast<f32x4*>(out + (size_t)tok * D_MODEL + col) = sum_partials(a, ksplit, tok, col);
+  *reinterpret_cast<f32x4*>(out + (size_t)tok * D_MODEL + col) = sum_partials<KS>(a, tok, col);
 }
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
@@ -318,27 +328,22 @@ static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int ksplit = 1) 
   return hipGetLastError();
 }
 
-// Epilogue of a split-K product: a.out holds the partials [ksplit][M][N].
-static hipError_t launch_splitk_epilogue(const GemmArgs& a, int ksplit, float* final_out,
-                                         hipStream_t s) {
+// Split-K product into the partial buffer `part` ([KS][M][N] fp32), then the
+// epilogue kernel. a.out is the final fp32 destination (out_proj) or unused.
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int KS>
+static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
+  static_assert((D_MODEL / BK) % KS == 0, "K steps must split evenly");
+  float* final_out = a.out;
+  a.out = part;
+  hipError_t e = launch_gemm<TOK, FEAT, WPN, WQN, STAGES, EPI_PARTIAL_F32>(a, s, KS);
+  if (e != hipSuccess) return e;
   const int threads = a.M * (a.N / 4);
   const dim3 grid((threads + 255) / 256);
   if (a.N == N_QKV)
-    hipLaunchKernelGGL(splitk_qkv_rope_kernel, grid, dim3(256), 0, s, a, ksplit);
+    hipLaunchKernelGGL(splitk_qkv_rope_kernel<KS>, grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(splitk_out_kernel, grid, dim3(256), 0, s, a, ksplit, final_out);
+    hipLaunchKernelGGL(splitk_out_kernel<KS>, grid, dim3(256), 0, s, a, final_out);
   return hipGetLastError();
-}
-
-// Split-K product into the partial buffer `part` ([ksplit][M][N] fp32), then
-// the epilogue kernel. a.out is the final fp32 destination (out_proj) or unused.
-template <int TOK, int FEAT, int WPN, int WQN, int STAGES>
-static hipError_t launch_gemm_splitk(GemmArgs a, float* part, int ksplit, hipStream_t s) {
-  float* final_out = a.out;
-  a.out = part;
-  hipError_t e = launch_gemm<TOK, FEAT, WPN, WQN, STAGES, EPI_PARTIAL_F32>(a, s, ksplit);
-  if (e != hipSuccess) return e;
-  return launch_splitk_epilogue(a, ksplit, final_out, s);
 }
 
 #ifndef GQA_GEMM_NO_LAUNCHERS
@@ -361,9 +366,12 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
   a.k_dst = k_dst; a.v_dst = v_dst; a.kv_bstride = kv_bstride; a.kv_rstride = kv_rstride;
   // Few tokens (decode): split K with a workspace, else thin weight strips and a
   // deep load ring; otherwise the largest tile that still fills the chip.
-  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4>(a, splitk, SPLITK, s);
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);
+  // 192-wide feature tiles give 512 workgroups at M = 2048 (256x256 tiles give
+  // 192, under one per CU)
+  if (M <= 8192) return launch_gemm<128, 192, 2, 2, 2, EPI_QKV_ROPE>(a, s);
   return launch_gemm<256, 256, 4, 2, 2, EPI_QKV_ROPE>(a, s);
 }
 
@@ -371,7 +379,7 @@ hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* 
                            float* splitk, hipStream_t s) {
   GemmArgs a{};
   a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1;
-  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4>(a, splitk, SPLITK, s);
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
   return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);

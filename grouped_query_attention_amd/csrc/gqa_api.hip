@@ -21,21 +21,24 @@ constexpr size_t KV_W = (size_t)N_KV * D_HEAD;  // 1024 features of K or V per t
 inline size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 inline bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
 
-// Prefill: Q_r, K_r, V, H (bf16), then the projections' split-reduction
-// scratch (only for M <= 64 tokens).
+// Prefill: Q_r, K_r, V, H (bf16), then one fp32 region shared, one kernel at a
+// time, by the projections' split-reduction partials (M <= 64 tokens only) and
+// the balanced causal attention's partials (few query tiles only).
 struct PrefillWs {
-  size_t q, k, v, h, splitk, total;
+  size_t q, k, v, h, part, total;
 };
 
-inline PrefillWs prefill_layout(long long M) {
+inline PrefillWs prefill_layout(int B, int T) {
   PrefillWs w{};
-  const size_t m = (size_t)M;
+  const size_t m = (size_t)B * T;   // <= GQA_MAX_TOKENS
   w.q = 0;
   w.k = w.q + align_up(m * D_MODEL * 2);
   w.v = w.k + align_up(m * KV_W * 2);
   w.h = w.v + align_up(m * KV_W * 2);
-  w.splitk = w.h + align_up(m * D_MODEL * 2);
-  w.total = w.splitk + align_up(gqa::gemm_splitk_bytes((int)M));   // M <= GQA_MAX_TOKENS
+  w.part = w.h + align_up(m * D_MODEL * 2);
+  const size_t proj = gqa::gemm_splitk_bytes((int)m);
+  const size_t attn = gqa::flash_partials_bytes(B, T, T, 1);
+  w.total = w.part + align_up(proj > attn ? proj : attn);
   return w;
 }
 
@@ -114,7 +117,12 @@ int gqa_rope_table(const int32_t* positions, int n, double theta, float* table) 
 
 size_t gqa_prefill_workspace_bytes(int B, int T) {
   if (!tokens_ok(B, T)) return 0;
-  return prefill_layout((long long)B * T).total;
+  return prefill_layout(B, T).total;
+}
+
+size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal) {
+  if (!tokens_ok(B, T) || kv_len != T || (causal != 0 && causal != 1)) return 0;
+  return gqa::flash_partials_bytes(B, T, kv_len, causal);
 }
 
 size_t gqa_decode_workspace_bytes(int B, int S_max) {
@@ -139,17 +147,20 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
 
 int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
                   const float* mask, int causal, int B, int T, int kv_len, gqa_bf16* h_out,
-                  void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!q_r || !k_r || !v || !h_out) return GQA_ERR_NULL;
   if (causal != 0 && causal != 1) return GQA_ERR_ARG;
   if (causal && mask) return GQA_ERR_ARG;
   if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
   if (kv_len != T) return GQA_ERR_UNSUPPORTED;
   if (misaligned(q_r) || misaligned(k_r) || misaligned(v) || misaligned(h_out) ||
-      (mask && misaligned(mask)))
+      (mask && misaligned(mask)) || misaligned(workspace))
     return GQA_ERR_ALIGN;
+  const size_t need = gqa::flash_partials_bytes(B, T, kv_len, causal);
+  if (workspace && workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  float* part = workspace && need ? static_cast<float*>(workspace) : nullptr;
   return hip_status(gqa::launch_flash_attention(q_r, k_r, v, (long long)kv_len * KV_W, mask,
-                                                causal, B, T, kv_len, 0, h_out,
+                                                causal, B, T, kv_len, 0, h_out, part,
                                                 (hipStream_t)stream));
 }
 
@@ -177,7 +188,7 @@ int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_
       (h_out && misaligned(h_out)))
     return GQA_ERR_ALIGN;
   const long long M = (long long)B * T;
-  const PrefillWs L = prefill_layout(M);
+  const PrefillWs L = prefill_layout(B, T);
   if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
 
@@ -186,17 +197,17 @@ int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_
   auto* k = reinterpret_cast<gqa_bf16*>(ws + L.k);
   auto* v = reinterpret_cast<gqa_bf16*>(ws + L.v);
   gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
-  float* splitk = L.total > L.splitk ? reinterpret_cast<float*>(ws + L.splitk) : nullptr;
+  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
   hipStream_t s = (hipStream_t)stream;
 
   hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
                                       (long long)T * D_MODEL, D_MODEL, k, v,
-                                      (long long)T * KV_W, KV_W, splitk, s);
+                                      (long long)T * KV_W, KV_W, part, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
-                                  h, s);
+                                  h, part, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, splitk, s));
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, part, s));
 }
 
 int gqa_decode_attention(const gqa_bf16* q_r, const gqa_bf16* k_cache,

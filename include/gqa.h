@@ -148,15 +148,26 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                  gqa_bf16* q_r, gqa_bf16* k_r, gqa_bf16* v, void* stream);
 
 /*
+ * Workspace bytes gqa_attention uses to balance a causal launch with few query
+ * tiles (the last query tile attends to every key tile, so with fewer than two
+ * 64-row tiles per CU the longest workgroup would set the time). 0 when the
+ * launch needs none (non-causal, or enough query tiles).
+ */
+size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal);
+
+/*
  * Stage 2 alone: grouped attention over already rotated queries and keys
  * ("All 13 steps": group map, scores, scale, mask, softmax, A·V_G, merge).
  *   q_r [B][T][32][128], k_r and v [B][kv_len][8][128]   bf16
  *   mask / causal as for gqa_block_forward (kv_len must equal T)
  *   h_out [B][T][32][128]   bf16 out
+ *   workspace   NULL (plain launch), or >= gqa_attention_workspace_bytes(B, T,
+ *               kv_len, causal) bytes of device memory (balanced launch; the
+ *               result is the same up to fp32 summation order)
  */
 int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
                   const float* mask, int causal, int B, int T, int kv_len,
-                  gqa_bf16* h_out, void* stream);
+                  gqa_bf16* h_out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Stage 3 alone: Δ = H·W_O (Merge and project page, Explanation; "All 13

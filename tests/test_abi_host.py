@@ -63,10 +63,20 @@ def test_rope_table_matches_oracle_trig():
 
 
 def test_workspace_sizes():
-    M = 3 * 129
+    M = 8 * 4096   # enough query tiles: no balanced-attention partials, no split reduction
     want = sum(((M * f * 2 + 255) // 256) * 256 for f in (4096, 1024, 1024, 4096))
-    assert gqa.prefill_workspace_bytes(3, 129) == want
+    assert gqa.prefill_workspace_bytes(8, 4096) == want
     assert gqa.prefill_workspace_bytes(0, 5) == 0
+    # few query tiles, causal: fp32 partials of the cut query tiles; the prefill
+    # workspace covers them; plain launches need none
+    att = gqa.attention_workspace_bytes(1, 2048, 2048, True)
+    assert att > 0 and att % (8 * (4 * 64 * 128 + 2 * 4 * 64) * 4) == 0
+    assert gqa.prefill_workspace_bytes(1, 2048) >= 2048 * 10240 * 2 + att
+    assert gqa.attention_workspace_bytes(1, 2048, 2048, False) == 0
+    assert gqa.attention_workspace_bytes(8, 4096, 4096, True) == 0
+    assert gqa.attention_workspace_bytes(1, 128, 128, True) == 0
+    # M <= 64 tokens: the projections' split-reduction partials (4 x M x 6144 fp32)
+    assert gqa.prefill_workspace_bytes(2, 30) >= 60 * 10240 * 2 + 4 * 60 * 6144 * 4
     # decode: Q_r and H (bf16 [B][4096] each) plus at least one fp32 partial
     # (O[4][128], max[4], sum[4]) per (sequence, KV head); more keys never need less
     for B in (1, 3, 64):
@@ -121,9 +131,14 @@ def test_stage_entries_reject():
     assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, None) == SHAPE
     assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, None, FAKE, 1, 4, FAKE, FAKE, FAKE, None) == NULL
     assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, MIS, FAKE, FAKE, None) == ALIGN
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 4, FAKE, None) == ARG
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 4, 5, FAKE, None) == UNSUPPORTED
-    assert lib.gqa_attention(FAKE, FAKE, None, None, 1, 1, 4, 4, FAKE, None) == NULL
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 4, FAKE, None, 0, None) == ARG
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 4, 5, FAKE, None, 0, None) == UNSUPPORTED
+    assert lib.gqa_attention(FAKE, FAKE, None, None, 1, 1, 4, 4, FAKE, None, 0, None) == NULL
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, MIS, 1 << 30,
+                             None) == ALIGN
+    need = gqa.attention_workspace_bytes(1, 2048, 2048, True)
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, FAKE, need - 1,
+                             None) == WORKSPACE
     assert lib.gqa_output_projection(FAKE, FAKE, 0, FAKE, None) == SHAPE
     assert lib.gqa_output_projection(FAKE, MIS, 3, FAKE, None) == ALIGN
     assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 2, 10, 11, FAKE, FAKE, 1 << 30, None) == SHAPE

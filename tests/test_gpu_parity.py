@@ -95,6 +95,27 @@ def test_attention_stage(B, T, causal):
     assert_close(bf16_to_np_f64(h), want, rel=STAGE_REL, what="H")
 
 
+@pytest.mark.parametrize("B,T", [(1, 1000), (1, 2048)])
+def test_attention_balanced_launch(B, T):
+    # few causal query tiles: cut tiles computed in pieces and merged; same
+    # result as the plain launch up to fp32 summation order, bitwise repeatable
+    print(f"[case] attention balanced B={B} T={T}", flush=True)
+    assert gqa.attention_workspace_bytes(B, T, T, True) > 0
+    q, k, v = _qkv_direct(700 + T, B, T)
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    h1 = gqa.attention(qd, kd, vd, causal=True)
+    h2 = gqa.attention(qd, kd, vd, causal=True)
+    hp = gqa.attention(qd, kd, vd, causal=True, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h1, h2)
+    want = O.grouped_attention(O.bf16_to_f64(q), O.bf16_to_f64(k), O.bf16_to_f64(v),
+                               O.causal_mask(T))
+    assert_close(bf16_to_np_f64(h1), want, rel=STAGE_REL, what="H balanced")
+    assert_close(bf16_to_np_f64(hp), want, rel=STAGE_REL, what="H plain")
+    d = (h1.float() - hp.float()).abs().max().item()
+    assert d <= 2 ** -4, d   # at most one bf16 ulp: |H| stays below 16
+
+
 def test_attention_explicit_mask():
     B, T = 2, 96
     print(f"[case] attention explicit mask B={B} T={T}", flush=True)
