@@ -560,6 +560,40 @@ struct DecodeArgs {
   int n_items;
 };
 
+// Merge of the split partials of (sequence b, KV head g), query head q = 4g + qq,
+// dims d0 .. d0 + 7: rescale each chunk's O and sum by its running max, add,
+// divide by the rescaled sum of the running sums; chunks in order. (Merging
+// inside the split kernel, by the last chunk of a head to finish, would need a
+// device-scope release/acquire per workgroup, which writes back and invalidates
+// the whole L2 each time and costs far more than this kernel.)
+__device__ __forceinline__ void decode_merge_dims(const DecodeArgs& a, int b, int g, int qq,
+                                                  int d0) {
+  constexpr int ND = 8;
+  const float* base = a.part + (size_t)(b * N_KV + g) * a.n_split * DC_PART;
+  float M = NEG_INF;
+  // unrolled so that several chunks' loads are in flight at once
+#pragma unroll 8
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * DC_PART + N_REP * D_HEAD + qq]);
+  float acc[ND], L = 0.f;
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = 0.f;
+#pragma unroll 4
+  for (int s = 0; s < a.n_split; ++s) {
+    const float* p = base + s * DC_PART;
+    const float ms = p[N_REP * D_HEAD + qq];
+    const float f = ms == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((ms - M) * SCALE_LOG2);
+#pragma unroll
+    for (int i = 0; i < ND; ++i) acc[i] += p[qq * D_HEAD + d0 + i] * f;
+    L += p[N_REP * D_HEAD + N_REP + qq] * f;
+  }
+  const float r = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* hp = a.h + ((size_t)b * N_HEADS + g * N_REP + qq) * D_HEAD + d0;
+  *reinterpret_cast<u32x4*>(hp) = u32x4{pack_bf16x2(acc[0] * r, acc[1] * r),
+                                        pack_bf16x2(acc[2] * r, acc[3] * r),
+                                        pack_bf16x2(acc[4] * r, acc[5] * r),
+                                        pack_bf16x2(acc[6] * r, acc[7] * r)};
+}
+
 // Persistent split-KV decode. Item j = (sequence b, chunk sp) covers keys
 // [sp*chunk, min(kv_len, (sp+1)*chunk)) of all 8 KV heads. Workgroup w takes
 // items w, w+G, w+2G, ... and streams their 16-key tiles of whole cache rows
@@ -571,7 +605,9 @@ struct DecodeArgs {
 // V^T operand is one transposed LDS read. Online softmax with a lazily moved
 // reference max; each wave writes an unnormalised fp32 partial per item.
 __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE];
+  // K/V tile ring, then two query slots (items alternate): [wave][4 heads][128]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE + 2 * DC_HG * 512];
+  uint16_t* const qslots = smem + DC_STAGES * 2 * DC_TILE;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -596,6 +632,13 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
     const int key_t = (item % a.n_split) * a.chunk + ld_t * DC_BN;
     const size_t seq = (size_t)(bh / (N_KV / DC_HG)) * a.S_max * DC_ROW + (bh % (N_KV / DC_HG)) * DC_TROW;
     uint16_t* st = smem + stage_ld * 2 * DC_TILE;
+    if (ld_t == 0) {
+      // first tile of an item: its queries go ahead of the tile, into slot ld_j & 1
+      // (lane l: query head 4g + l/16, dims 8(l%16) .. +7 of this wave's KV head g)
+      const int b = bh / (N_KV / DC_HG), g = (bh % (N_KV / DC_HG)) * DC_HG + w;
+      dma16((const void*)(a.q + ((size_t)b * N_HEADS + g * N_REP) * D_HEAD + lane * 8),
+            qslots + ((ld_j & 1) * DC_HG + w) * 512);
+    }
 #pragma unroll
     for (int j = 0; j < DC_NI_W; ++j) {
       // instruction i: the 1-KiB piece ii of the K (i < DC_NI) or V tile; lane l
@@ -632,21 +675,10 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
     const int nt = item_tiles(item);
 
     // Query fragments (MFMA B operand, 16x16x32): column l16 = query head 4g + l16
-    // (zero for l16 >= 4), k-step s covers d = 32s + 8*lg .. +7.
+    // (zero for l16 >= 4), k-step s covers d = 32s + 8*lg .. +7. Read from the
+    // item's query slot once its first tile is resident (the query load went
+    // ahead of that tile's loads, and loads complete in order).
     u32x4 qf[4];
-    {
-      const bool ok = l16 < N_REP;
-      const uint16_t* qrow = a.q + ((size_t)b * N_HEADS + g * N_REP + (ok ? l16 : 0)) * D_HEAD + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qf[s] = ok ? ld16(qrow + 32 * s) : z;
-      }
-    }
-    // vmcnt is one in-order counter shared with the direct-to-LDS stream: wait for
-    // the query loads here, once per item, or the compiler waits for every load in
-    // flight before the first use of qf in each tile.
-    wait_vmcnt<0>();
     f32x4 o[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[i] = f32x4{};
@@ -657,6 +689,15 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
       // tile done-1, whose stage the next load reuses
       wait_keep<DC_NI_W, DC_STAGES - 2>(min(DC_STAGES - 2, issued - done - 1));
       barrier_no_fence();
+      if (t == 0) {
+        const uint16_t* qrow = qslots + ((j & 1) * DC_HG + w) * 512 + (l16 & 3) * D_HEAD + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 v = ld16(qrow + 32 * s);
+          qf[s] = l16 < N_REP ? v : z;
+        }
+      }
       if (issued < total_tiles) { issue_next(); ++issued; }
 
       const uint16_t* sk = smem + (done % DC_STAGES) * 2 * DC_TILE;
@@ -716,29 +757,11 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
   }
 }
 
-// One workgroup per (sequence, query head): rescale and sum the split partials.
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a) {
-  const int b = blockIdx.x / N_HEADS, h = blockIdx.x % N_HEADS;
-  const int g = h / N_REP, q = h % N_REP;
-  const int d = threadIdx.x;
-  const float* base = a.part + (size_t)(b * N_KV + g) * a.n_split * DC_PART;
-  // unrolled so that several splits' loads are in flight at once
-  float M = NEG_INF;
-#pragma unroll 8
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, base[s * DC_PART + N_REP * D_HEAD + q]);
-  float acc = 0.f, L = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < a.n_split; ++s) {
-    const float* p = base + s * DC_PART;
-    const float ms = p[N_REP * D_HEAD + q];
-    const float f = ms == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((ms - M) * SCALE_LOG2);
-    acc += p[q * D_HEAD + d] * f;
-    L += p[N_REP * D_HEAD + N_REP + q] * f;
-  }
-  const float r = L > 0.f ? acc / L : 0.f;
-  f32x2 v = {r, 0.f};
-  bf16x2 bv = __builtin_convertvector(v, bf16x2);
-  a.h[((size_t)b * N_HEADS + h) * D_HEAD + d] = (uint16_t)(__builtin_bit_cast(uint32_t, bv) & 0xffffu);
+// One wave per (sequence, KV head): rescale and sum the split partials of its
+// four query heads; lane l takes query head 4g + l/16, dims 8(l%16) .. +7.
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int b = blockIdx.x / N_KV, g = blockIdx.x % N_KV;
+  decode_merge_dims(a, b, g, threadIdx.x >> 4, (threadIdx.x & 15) * 8);
 }
 
 size_t decode_partials_bytes(int B, int S_max) {
@@ -768,7 +791,7 @@ hipError_t launch_decode_attention(const uint16_t* q_r, const uint16_t* k_cache,
   hipLaunchKernelGGL(decode_splitkv_kernel, dim3((unsigned)grid), dim3(DC_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * N_HEADS)), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * N_KV)), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
