@@ -33,6 +33,16 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PARAMS_PER_BLOCK = 41_943_040  # W_Q + W_K + W_V + W_O
 
+# HBM-side bytes per launch of each headline stage (B=1, T=2048), FETCH_SIZE +
+# WRITE_SIZE from two rocprofv3 --pmc runs, scaled by a 1 GiB copy's counters;
+# see profiles/hbm_fetch_write_prefill_B1_T2048.md. Valid for the kernel
+# instantiations named here only: re-measure when they change.
+PROFILED_TRAFFIC = {
+    "qkv_rope": {"kernel": "gemm_nt_kernel<128, 192, 2, 2, 2, 0, 64>", "bytes": 213.4e6},
+    "attention": {"kernel": "flash_fwd_kernel + flash_merge_kernel", "bytes": 110.6e6},
+    "out_proj": {"kernel": "gemm_nt_kernel<128, 128, 2, 2, 2, 1, 64>", "bytes": 168.0e6},
+}
+
 
 def prefill_flops(B, T, start_pos=0):
     """Algorithmic flops: the four projections plus 4*32*128 per unmasked (q, k) pair."""
@@ -87,6 +97,26 @@ class Bench:
         wall = (time.perf_counter() - t0) * 1e3 / steps
         return e0.elapsed_time(e1) / steps, wall
 
+    def time_cold(self, fn, steps):
+        """Median per-step time with the caches cleared before each step: a
+        512 MiB buffer is read (a sum) outside the timed events, so weights and
+        activations come from HBM as they would after the rest of a layer."""
+        torch = self.torch
+        if not hasattr(self, "_flush"):
+            self._flush = torch.ones((512 << 20) // 4, dtype=torch.float32, device=self.dev)
+        ts = []
+        for _ in range(steps):
+            self._flush.sum()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
     # ---------------- headline: prefill B=1 T=2048 ----------------
     def headline(self):
         gqa, args = self.gqa, self.args
@@ -104,6 +134,8 @@ class Bench:
         F = prefill_flops(B, T)
         value = F / (ms * 1e-3) / 1e12
         self.log(f"[bench] prefill C2: {ms:.4f} ms/step (wall {wall_ms:.4f}), {value:.1f} TFLOP/s")
+        cold_ms = self.time_cold(step, args.steps)
+        self.log(f"[bench] prefill C2 cold caches: {cold_ms:.4f} ms/step")
 
         # per-kernel timing (stage entries launch exactly the kernels of the step)
         q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
@@ -128,9 +160,13 @@ class Bench:
             kern[name]["frac"] = kern[name]["tflops"] / PEAK_BF16_TFLOPS
             self.log(f"[bench]   {name}: {kms:.4f} ms, {kern[name]['tflops']:.1f} TFLOP/s")
         dom = max(kern, key=lambda k: kern[k]["ms"])
+        prof = PROFILED_TRAFFIC.get(dom)
         roofline = {"bound": "mfma", "kernel": kern[dom]["kernel"], "stage": dom,
                     "achieved": round(kern[dom]["tflops"], 2), "peak": PEAK_BF16_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(kern[dom]["frac"], 4), "traffic": None,
+                    "unit": "TFLOP/s", "frac": round(kern[dom]["frac"], 4),
+                    "traffic": prof["bytes"] if prof else None,
+                    "traffic_unit": "bytes per launch (HBM-side, rocprofv3 FETCH_SIZE+WRITE_SIZE)",
+                    "traffic_kernel": prof["kernel"] if prof else None,
                     "flops_per_launch": sf[dom], "avg_launch_ms": round(kern[dom]["ms"], 5)}
 
         result = {
@@ -142,6 +178,9 @@ class Bench:
                        "B": B, "T": T, "d": 4096, "q_heads": 32, "kv_heads": 8, "d_head": 128,
                        "rope_theta": 500000.0, "flops_per_step": F,
                        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+            "cold_cache": {"ms_per_step": round(cold_ms, 5),
+                           "TFLOP/s": round(F / (cold_ms * 1e-3) / 1e12, 2),
+                           "note": "median step with a 512 MiB read between steps"},
             "roofline": roofline,
             "kernels": {k: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                             for kk, vv in d.items()} for k, d in kern.items()},
@@ -163,6 +202,7 @@ class Bench:
         dws = torch.empty(gqa.decode_workspace_bytes(Bd, S), dtype=torch.uint8, device=self.dev)
         dstep = lambda: gqa.decode_forward(dx, *dw, drope, kc, vc, sp, out=dout, workspace=dws)
         dms, _ = self.time_steps(dstep, args.steps, args.warmup)
+        dcold = self.time_cold(dstep, args.steps)
         nbytes = decode_bytes(Bd, S)
         qd = torch.zeros((Bd, 32, 128), dtype=torch.bfloat16, device=self.dev)
         hd = torch.empty_like(qd)
@@ -174,6 +214,8 @@ class Bench:
             "ms": round(dms, 5), "GB/s": round(nbytes / (dms * 1e-3) / 1e9, 1),
             "frac_of_hbm": round(nbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "bytes_per_step": nbytes,
+            "cold_cache": {"ms": round(dcold, 5),
+                           "GB/s": round(nbytes / (dcold * 1e-3) / 1e9, 1)},
             "attention_kernel": {"kernel": "decode_splitkv_kernel+decode_merge_kernel",
                                  "ms": round(ams, 5),
                                  "GB/s": round(kv_bytes / (ams * 1e-3) / 1e9, 1),

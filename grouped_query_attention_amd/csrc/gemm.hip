@@ -56,12 +56,20 @@ struct GemmArgs {
   float* out;
 };
 
-// Chunk permutation of row r: a bijection on r & 7 for any 8 aligned rows (so 8
-// lanes reading one chunk of rows r0..r0+7 hit 8 distinct 16-byte slots of a
-// 128-byte bank window), which also differs between rows r and r + 8 (so 16
-// lanes reading rows r0..r0+15 hit 16 distinct slots of a 256-byte window).
-__device__ __forceinline__ int rperm(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz(int r, int c) { return r * BK + ((c ^ rperm(r)) << 3); }
+// Chunk permutation of row r for LDS rows of KB bf16 (KB/8 chunks of 16 bytes).
+// The 16 lanes of a fragment read take one chunk c of 16 consecutive rows and
+// must hit the 16 distinct 16-byte slots of a 256-byte bank window.
+//  * KB = 64 (128-byte rows, 2 per window): a bijection on r & 7 for any 8
+//    aligned rows that also differs between rows r and r + 8.
+//  * KB = 32 (64-byte rows, 4 per window): rows r mod 4 fill the window's four
+//    64-byte quarters and (r >> 2) & 3 picks the chunk inside each.
+template <int KB>
+__device__ __forceinline__ int rperm(int r) {
+  if constexpr (KB == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;
+}
+template <int KB>
+__device__ __forceinline__ int swz(int r, int c) { return r * KB + ((c ^ rperm<KB>(r)) << 3); }
 
 // Maps a linear workgroup id to (token tile, feature tile): workgroups are
 // dealt round-robin to the 8 XCDs, so ids are first regrouped so that each
@@ -103,8 +111,12 @@ __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int f) 
   return a.w0 + (size_t)f * D_MODEL;
 }
 
-template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
 struct GemmCfg {
+  static_assert(KB == 64 || KB == 32, "K step");
+  static constexpr int BK = KB;
+  static constexpr int CPR = KB / 8;                   // 16-byte chunks per LDS row
+  static constexpr int RPI = 512 / KB;                 // LDS rows per 1 KiB load instruction
   static constexpr bool SWAP = (EPI == EPI_QKV_ROPE);
   static constexpr int PR = SWAP ? FEAT : TOK;   // MFMA A operand rows
   static constexpr int QR = SWAP ? TOK : FEAT;   // MFMA B operand rows
@@ -114,7 +126,7 @@ struct GemmCfg {
   static constexpr int NP = WP / 32, NQ = WQ / 32;
   static constexpr int STAGE_ELEMS = (PR + QR) * BK;
   static constexpr int LDS_BYTES = STAGES * STAGE_ELEMS * 2;
-  static constexpr int NI = (PR + QR) / 8;             // 1 KiB load instructions per stage
+  static constexpr int NI = (PR + QR) / RPI;           // 1 KiB load instructions per stage
   static constexpr int NI_W = NI / NW;                 // per wave
   static_assert(NI % NW == 0, "load instructions must split evenly across waves");
   static_assert(WP % 32 == 0 && WQ % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
@@ -122,11 +134,12 @@ struct GemmCfg {
   static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
 };
 
-template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
 __global__ __launch_bounds__(64 * WPN * WQN)
 void gemm_nt_kernel(GemmArgs a) {
-  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI>;
+  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>;
   constexpr int PR = C::PR, QR = C::QR, NP = C::NP, NQ = C::NQ;
+  constexpr int BK = C::BK;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * C::STAGE_ELEMS];
 
   const int tid = threadIdx.x;
@@ -149,14 +162,15 @@ void gemm_nt_kernel(GemmArgs a) {
   const int tok_last = a.M - m0 - 1;   // rows past it are clamped (their outputs are discarded)
 
   // This lane's source pointers for its NI_W load instructions (K offset added per step).
-  // Instruction i covers LDS rows 8i..8i+7 of the stage (P rows first, then Q rows);
-  // lane l writes row 8i + (l >> 3), physical chunk l & 7 = logical chunk (l & 7) ^ rperm(row).
+  // Instruction i covers LDS rows RPI*i .. RPI*i + RPI-1 of the stage (P rows first,
+  // then Q rows); lane l writes row RPI*i + l / CPR, physical chunk l % CPR, which
+  // holds logical chunk (l % CPR) ^ rperm(row).
   const uint16_t* src[C::NI_W];
 #pragma unroll
   for (int j = 0; j < C::NI_W; ++j) {
     const int i = wave + j * C::NW;
-    int row = 8 * i + (lane >> 3);
-    const int lc = (lane & 7) ^ rperm(row);
+    int row = C::RPI * i + lane / C::CPR;
+    const int lc = (lane % C::CPR) ^ rperm<BK>(row);
     const bool is_p = row < PR;
     const int r = is_p ? row : row - PR;
     const bool is_tok = C::SWAP ? !is_p : is_p;
@@ -196,9 +210,9 @@ void gemm_nt_kernel(GemmArgs a) {
     auto read_frags = [&](int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
       const int ch = kk * 2 + lhalf;
 #pragma unroll
-      for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz(wp * C::WP + i * 32 + lrow, ch));
+      for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz<BK>(wp * C::WP + i * 32 + lrow, ch));
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz(wq * C::WQ + j * 32 + lrow, ch));
+      for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 32 + lrow, ch));
     };
     read_frags(0, af[0], bf[0]);
 #pragma unroll
@@ -319,11 +333,11 @@ __global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, float* out)
   *reinterpret_cast<f32x4*>(out + (size_t)tok * D_MODEL + col) = sum_partials<KS>(a, tok, col);
 }
 
-template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI>
+template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int ksplit = 1) {
-  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI>;
+  using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>;
   const int tiles = ((a.M + TOK - 1) / TOK) * (a.N / FEAT);
-  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI>), dim3(tiles, ksplit),
+  hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>), dim3(tiles, ksplit),
                      dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
 }
