@@ -5,7 +5,8 @@ Headline: prefill B=1, T=2048, causal, the whole block (fused QKV projection
 with rotation, grouped flash attention, output projection) per step, in
 TFLOP/s of algorithmic work (only unmasked query/key pairs count). Also
 measured in the same run: decode (B=64, one token at position 8191 over a
-bf16 KV cache of 8192 rows) in HBM GB/s, and prefill at B=8, T=4096 and at
+bf16 KV cache of 8192 rows) in HBM GB/s, chunked prefill (B=1, 2048 new
+positions after 2048 cached ones), and prefill at B=8, T=4096 and at
 B=1, T=131072.
 
 Prints one JSON line. Inputs are seeded synthetic bf16 values resident in HBM
@@ -15,7 +16,7 @@ time in the headline step, timed with HIP events on the stream it runs on;
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-       python bench.py --only decode|prefill_B8_T4096|prefill_B1_T131072
+       python bench.py --only decode|chunk|prefill_B8_T4096|prefill_B1_T131072
 """
 
 import argparse
@@ -247,6 +248,32 @@ class Bench:
         del px, pw, pout, pws
         torch.cuda.empty_cache()
 
+    # ---------------- chunked prefill into a KV cache ----------------
+    def chunk(self, extra):
+        """B=1: 2048 new positions at start_pos 2048 over a cache of 4096 rows."""
+        torch, gqa, args = self.torch, self.gqa, self.args
+        B, T, sp, S = 1, 2048, 2048, 4096
+        self.log(f"[bench] chunked prefill B={B} T={T} start_pos={sp}: generating inputs")
+        inp = self.gi.make_block_inputs(6, B, T, cache_len=S)
+        x = self.up(inp.x)
+        w = [self.up(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo)]
+        kc, vc = self.up(inp.k_cache), self.up(inp.v_cache)
+        del inp
+        rope = torch.from_numpy(gqa.rope_table(np.arange(sp, sp + T))).to(self.dev)
+        out = torch.empty((B, T, 4096), dtype=torch.float32, device=self.dev)
+        ws = torch.empty(gqa.chunk_workspace_bytes(B, T, sp), dtype=torch.uint8, device=self.dev)
+        step = lambda: gqa.chunk_forward(x, *w, rope, kc, vc, sp, out=out, workspace=ws)
+        ms, _ = self.time_steps(step, args.steps, args.warmup)
+        F = prefill_flops(B, T, sp)
+        tf = F / (ms * 1e-3) / 1e12
+        extra[f"chunk_B{B}_T{T}_start{sp}"] = {
+            "ms": round(ms, 5), "TFLOP/s": round(tf, 1),
+            "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4), "flops_per_step": F,
+            "kv_len": sp + T}
+        self.log(f"[bench] chunked prefill: {ms:.4f} ms, {tf:.1f} TFLOP/s")
+        del kc, vc, ws
+        torch.cuda.empty_cache()
+
     def prefill_b8(self, extra):
         self.prefill(extra, 8, 4096, 3, max(3, self.args.steps // 4))
 
@@ -295,7 +322,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--only", choices=["decode", "prefill_B8_T4096", "prefill_B1_T131072"],
+    ap.add_argument("--only", choices=["decode", "chunk", "prefill_B8_T4096",
+                                       "prefill_B1_T131072"],
                     help="run just this one workload and print its figures (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (3 times), for "
@@ -310,7 +338,7 @@ def main():
     if args.calibrate_copy:
         b.calibrate_copy(args.calibrate_copy)
         return
-    others = {"decode": b.decode, "prefill_B8_T4096": b.prefill_b8,
+    others = {"decode": b.decode, "chunk": b.chunk, "prefill_B8_T4096": b.prefill_b8,
               "prefill_B1_T131072": b.prefill_long}
     if args.only:
         extra = {}

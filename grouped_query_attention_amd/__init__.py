@@ -53,6 +53,8 @@ def _load():
         "gqa_prefill_workspace_bytes": (Z, [I, I]),
         "gqa_decode_workspace_bytes": (Z, [I, I]),
         "gqa_attention_workspace_bytes": (Z, [I, I, I, I]),
+        "gqa_chunk_workspace_bytes": (Z, [I, I, I]),
+        "gqa_chunk_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_block_forward": (I, [P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_decode_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P, Z, P]),
         "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, P]),
@@ -76,7 +78,8 @@ def lib():
 def exported_symbols():
     return ["gqa_status_string", "gqa_dims", "gqa_rope_table", "gqa_prefill_workspace_bytes",
             "gqa_decode_workspace_bytes", "gqa_attention_workspace_bytes",
-            "gqa_block_forward", "gqa_decode_forward",
+            "gqa_chunk_workspace_bytes", "gqa_block_forward", "gqa_chunk_forward",
+            "gqa_decode_forward",
             "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention"]
 
 
@@ -139,6 +142,10 @@ def decode_workspace_bytes(B: int, S_max: int) -> int:
     return int(_load().gqa_decode_workspace_bytes(B, S_max))
 
 
+def chunk_workspace_bytes(B: int, T: int, start_pos: int) -> int:
+    return int(_load().gqa_chunk_workspace_bytes(B, T, int(start_pos)))
+
+
 def attention_workspace_bytes(B: int, T: int, kv_len: int, causal: bool = True) -> int:
     return int(_load().gqa_attention_workspace_bytes(B, T, kv_len, int(bool(causal))))
 
@@ -193,6 +200,33 @@ def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int
         _ptr(v_cache), B, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
     _check("gqa_decode_forward", st)
+    return out
+
+
+def chunk_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,
+                  out=None, h_out=None, workspace=None, stream=None):
+    """T new positions per sequence at start_pos .. start_pos+T-1 over a KV cache
+    holding positions 0 .. start_pos-1; x [B, T, 4096]; returns out [B, T, 4096] fp32.
+
+    Writes the new rotated keys and values into cache slots start_pos .. start_pos+T-1.
+    """
+    import torch
+    B, T, _ = x.shape
+    S_max = k_cache.shape[1]
+    _req(x, torch.bfloat16, (B, T, D_MODEL), "x")
+    _req(rope, torch.float32, (T, N_PAIRS, 2), "rope")
+    _req(k_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "k_cache")
+    _req(v_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "v_cache")
+    if out is None:
+        out = torch.empty((B, T, D_MODEL), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(chunk_workspace_bytes(B, T, start_pos), dtype=torch.uint8,
+                                device=x.device)
+    st = _load().gqa_chunk_forward(
+        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
+        _ptr(v_cache), B, T, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("gqa_chunk_forward", st)
     return out
 
 

@@ -480,9 +480,9 @@ bool flash_plan(int B, int T, int kv_len, int q_pos0, int causal, FlashPlan& p) 
 
 }  // namespace
 
-size_t flash_partials_bytes(int B, int T, int kv_len, int causal) {
+size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal) {
   FlashPlan p;
-  if (!flash_plan(B, T, kv_len, 0, causal, p)) return 0;
+  if (!flash_plan(B, T, kv_len, q_pos0, causal, p)) return 0;
   return (size_t)p.n_slots * B * N_KV * FA_PART * sizeof(float);
 }
 

@@ -197,16 +197,16 @@ void gemm_nt_kernel(GemmArgs a) {
     if (s < NK) issue(s, s);
 
   const int lrow = lane & 31, lhalf = lane >> 5;
+  // fragments double-buffered in registers: reads of slice kk+1 overlap the MFMAs
+  // of kk (declared outside the step loop: the generated loop is faster)
+  u32x4 af[2][NP], bf[2][NQ];
   for (int kt = 0; kt < NK; ++kt) {
     // wait for this step's loads; keep the later steps' loads (at most STAGES-2) in flight
     wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 1 - kt));
     barrier_no_fence();
-    if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
 
     const uint16_t* sp = smem + (kt % STAGES) * C::STAGE_ELEMS;
     const uint16_t* sq = sp + PR * BK;
-    // fragments double-buffered in registers: reads of slice kk+1 overlap the MFMAs of kk
-    u32x4 af[2][NP], bf[2][NQ];
     auto read_frags = [&](int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
       const int ch = kk * 2 + lhalf;
 #pragma unroll
@@ -215,6 +215,8 @@ void gemm_nt_kernel(GemmArgs a) {
       for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 32 + lrow, ch));
     };
     read_frags(0, af[0], bf[0]);
+    // the next stage's loads go out while the first fragment reads are in flight
+    if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       // Issue the reads of slice kk+1 before the MFMAs of slice kk and keep the

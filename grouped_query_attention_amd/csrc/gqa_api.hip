@@ -37,7 +37,25 @@ inline PrefillWs prefill_layout(int B, int T) {
   w.h = w.v + align_up(m * KV_W * 2);
   w.part = w.h + align_up(m * D_MODEL * 2);
   const size_t proj = gqa::gemm_splitk_bytes((int)m);
-  const size_t attn = gqa::flash_partials_bytes(B, T, T, 1);
+  const size_t attn = gqa::flash_partials_bytes(B, T, T, 0, 1);
+  w.total = w.part + align_up(proj > attn ? proj : attn);
+  return w;
+}
+
+// Chunked prefill: Q_r, H (bf16; K_r and V go to the cache), then one fp32
+// region for the split-K partials (M <= 64) or the balanced attention's partials.
+struct ChunkWs {
+  size_t q, h, part, total;
+};
+
+inline ChunkWs chunk_layout(int B, int T, int start_pos) {
+  ChunkWs w{};
+  const size_t m = (size_t)B * T;   // <= GQA_MAX_TOKENS
+  w.q = 0;
+  w.h = align_up(m * D_MODEL * 2);
+  w.part = w.h + align_up(m * D_MODEL * 2);
+  const size_t proj = gqa::gemm_splitk_bytes((int)m);
+  const size_t attn = gqa::flash_partials_bytes(B, T, start_pos + T, start_pos, 1);
   w.total = w.part + align_up(proj > attn ? proj : attn);
   return w;
 }
@@ -122,7 +140,12 @@ size_t gqa_prefill_workspace_bytes(int B, int T) {
 
 size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal) {
   if (!tokens_ok(B, T) || kv_len != T || (causal != 0 && causal != 1)) return 0;
-  return gqa::flash_partials_bytes(B, T, kv_len, causal);
+  return gqa::flash_partials_bytes(B, T, kv_len, 0, causal);
+}
+
+size_t gqa_chunk_workspace_bytes(int B, int T, int start_pos) {
+  if (!tokens_ok(B, T) || start_pos < 0 || (long long)start_pos + T > (1LL << 30)) return 0;
+  return chunk_layout(B, T, start_pos).total;
 }
 
 size_t gqa_decode_workspace_bytes(int B, int S_max) {
@@ -156,7 +179,7 @@ int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
   if (misaligned(q_r) || misaligned(k_r) || misaligned(v) || misaligned(h_out) ||
       (mask && misaligned(mask)) || misaligned(workspace))
     return GQA_ERR_ALIGN;
-  const size_t need = gqa::flash_partials_bytes(B, T, kv_len, causal);
+  const size_t need = gqa::flash_partials_bytes(B, T, kv_len, 0, causal);
   if (workspace && workspace_bytes < need) return GQA_ERR_WORKSPACE;
   float* part = workspace && need ? static_cast<float*>(workspace) : nullptr;
   return hip_status(gqa::launch_flash_attention(q_r, k_r, v, (long long)kv_len * KV_W, mask,
@@ -206,6 +229,44 @@ int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
                                   h, part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, part, s));
+}
+
+int gqa_chunk_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                      gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int T, int S_max,
+                      int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st != GQA_OK) return st;
+  if (!tokens_ok(B, T) || S_max < 1 || start_pos < 0 || (long long)start_pos + T > S_max)
+    return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
+      misaligned(out) || (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const ChunkWs L = chunk_layout(B, T, start_pos);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  const long long M = (long long)B * T;
+  const long long cache_bstride = (long long)S_max * KV_W;
+
+  // new keys and values go straight into cache slots start_pos .. start_pos+T-1
+  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
+                                      (long long)T * D_MODEL, D_MODEL,
+                                      k_cache + (size_t)start_pos * KV_W,
+                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, KV_W,
+                                      part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_flash_attention(q, k_cache, v_cache, cache_bstride, nullptr, 1, B, T,
+                                  start_pos + T, start_pos, h, part, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, part, s));
 }

@@ -109,6 +109,37 @@ int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_
                       float* out, gqa_bf16* h_out, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* Workspace bytes gqa_chunk_forward needs for B sequences of T new positions
+ * starting at start_pos. */
+size_t gqa_chunk_workspace_bytes(int B, int T, int start_pos);
+
+/*
+ * Chunked prefill into a KV cache: T new positions per sequence, at positions
+ * start_pos .. start_pos+T-1, after a cache that already holds positions
+ * 0 .. start_pos-1. Grouped-query attention page, "All 13 steps" with the
+ * model.py excerpt's cache semantics: row i of the new block is token
+ * start_pos + i and sees keys 0 .. start_pos + i (the excerpt's mask: zeros
+ * for the cached columns, then the causal triangle).
+ *   x       [B][T][4096]           bf16  block input of the new positions
+ *   w_q, w_k, w_v, w_o                   as for gqa_block_forward
+ *   rope    [T][64][2]             f32   (cos, sin) at positions start_pos + t
+ *   k_cache [B][S_max][8][128]     bf16  rotated keys of positions 0..start_pos-1;
+ *                                        slots start_pos..start_pos+T-1 are
+ *                                        overwritten with the new rotated keys
+ *   v_cache [B][S_max][8][128]     bf16  values, same slots
+ *   B, T, S_max, start_pos               B >= 1, T >= 1, start_pos >= 0,
+ *                                        start_pos + T <= S_max, B*T <= GQA_MAX_TOKENS
+ *   out     [B][T][4096]           f32   Δ
+ *   h_out   [B][T][32][128]        bf16  merged head outputs, or NULL
+ *   workspace                            >= gqa_chunk_workspace_bytes(B, T, start_pos)
+ * start_pos = 0 is an ordinary causal prefill that also fills the cache.
+ */
+int gqa_chunk_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                      gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int T, int S_max,
+                      int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Workspace bytes gqa_decode_forward needs for B sequences and a cache of S_max rows. */
 size_t gqa_decode_workspace_bytes(int B, int S_max);
 

@@ -126,6 +126,37 @@ def test_decode_forward_rejects(kw, want):
     assert _dec(**kw) == want
 
 
+def _chk(**kw):
+    a = dict(x=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, wo=FAKE, rope=FAKE, kc=FAKE, vc=FAKE, B=2,
+             T=16, S=64, sp=48, out=FAKE, h=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return gqa.lib().gqa_chunk_forward(a["x"], a["wq"], a["wk"], a["wv"], a["wo"], a["rope"],
+                                       a["kc"], a["vc"], a["B"], a["T"], a["S"], a["sp"],
+                                       a["out"], a["h"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(kc=None), NULL), (dict(x=None), NULL), (dict(wo=None), NULL), (dict(out=None), NULL),
+    (dict(sp=49), SHAPE), (dict(sp=-1), SHAPE), (dict(T=0), SHAPE), (dict(B=0), SHAPE),
+    (dict(S=0), SHAPE), (dict(vc=MIS), ALIGN), (dict(h=MIS), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE), (dict(ws=MIS), ALIGN),
+])
+def test_chunk_forward_rejects(kw, want):
+    assert _chk(**kw) == want
+
+
+def test_chunk_workspace_sizes():
+    # Q_r and H (bf16) plus the shared fp32 region; at start_pos 0 with enough query
+    # tiles it is the prefill workspace without K_r and V
+    assert gqa.chunk_workspace_bytes(8, 4096, 0) == 2 * 8 * 4096 * 4096 * 2
+    assert gqa.chunk_workspace_bytes(0, 4, 0) == 0
+    assert gqa.chunk_workspace_bytes(1, 4, -1) == 0
+    # one position per sequence: split-K partials (4 x B x 6144 fp32)
+    assert gqa.chunk_workspace_bytes(2, 1, 299) >= 2 * 2 * 4096 * 2 + 4 * 2 * 6144 * 4
+    # few query tiles at an offset: the balanced plan's partials
+    assert gqa.chunk_workspace_bytes(1, 1024, 512) > 2 * 1024 * 4096 * 2
+
+
 def test_stage_entries_reject():
     lib = gqa.lib()
     assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, None) == SHAPE

@@ -194,6 +194,60 @@ def test_block_forward_c5_sampled():
     assert_close(hh, ref["h"], rel=BLOCK_H_REL, mabs=BLOCK_H_ABS, what="H C5")
 
 
+# --- chunked prefill into a KV cache ----------------------------------------------------
+
+def _chunk(x_bits, inp, k_cache, v_cache, start_pos, h=False):
+    """x_bits [B, T, 4096] bf16 bits; caches are device tensors (updated in place)."""
+    B, T = x_bits.shape[:2]
+    x = to_dev_bf16(x_bits)
+    wq, wk, wv, wo = _weights(inp)
+    rope = to_dev_f32(gqa.rope_table(np.arange(start_pos, start_pos + T)))
+    hb = torch.empty((B, T, 32, 128), dtype=torch.bfloat16, device=dev()) if h else None
+    out = gqa.chunk_forward(x, wq, wk, wv, wo, rope, k_cache, v_cache, start_pos, h_out=hb)
+    torch.cuda.synchronize()
+    return out, hb
+
+
+# (1, 1024, 2048, 512) runs the balanced attention plan with a position offset;
+# (3, 20, 64, 44) ends exactly at S_max; (2, 1, 300, 299) is a one-position chunk
+# (split-K projections).
+@pytest.mark.parametrize("B,T,S_max,start_pos", [(2, 37, 256, 100), (1, 128, 128, 0),
+                                                 (1, 1024, 2048, 512), (3, 20, 64, 44),
+                                                 (2, 1, 300, 299)])
+def test_chunk_forward(B, T, S_max, start_pos):
+    print(f"[case] chunk B={B} T={T} S_max={S_max} start_pos={start_pos}", flush=True)
+    inp = gi.make_block_inputs(60 + T + start_pos, B, T, cache_len=S_max)
+    kc, vc = to_dev_bf16(inp.k_cache), to_dev_bf16(inp.v_cache)
+    out, h = _chunk(inp.x, inp, kc, vc, start_pos, h=True)
+    ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8, start_pos=start_pos,
+                          k_cache=inp.k_cache, v_cache=inp.v_cache)
+    assert_close(f32_to_np_f64(out), ref["delta"], what="Δ chunk")
+    assert_close(bf16_to_np_f64(h).reshape(B, T, 4096), ref["h"], rel=BLOCK_H_REL,
+                 mabs=BLOCK_H_ABS, what="H chunk")
+    kc_np, vc_np = bf16_to_np_f64(kc), bf16_to_np_f64(vc)
+    new = slice(start_pos, start_pos + T)
+    assert_close(kc_np[:, new], ref["k_r"], rel=STAGE_REL, what="cache K slots")
+    assert_close(vc_np[:, new], ref["v"], rel=STAGE_REL, what="cache V slots")
+    keep = np.ones(S_max, bool)
+    keep[new] = False
+    assert np.array_equal(kc_np[:, keep], O.bf16_to_f64(inp.k_cache)[:, keep])
+    assert np.array_equal(vc_np[:, keep], O.bf16_to_f64(inp.v_cache)[:, keep])
+
+
+def test_two_chunks_equal_one_prefill():
+    # a prefill of 300 positions into an empty cache, then a chunk of 200 more,
+    # reproduces rows 300..499 of the causal prefill of all 500 positions
+    print("[case] chunk 300 then 200 vs prefill of 500", flush=True)
+    T1, T2, S_max = 300, 200, 512
+    inp = gi.make_block_inputs(77, 1, T1 + T2)
+    kc = torch.zeros((1, S_max, 8, 128), dtype=torch.bfloat16, device=dev())
+    vc = torch.zeros_like(kc)
+    _chunk(inp.x[:, :T1], inp, kc, vc, 0)
+    out2, _ = _chunk(inp.x[:, T1:], inp, kc, vc, T1)
+    ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)
+    assert_close(f32_to_np_f64(out2), ref["delta"][:, T1:], what="Δ second chunk")
+
+
 # --- decode ------------------------------------------------------------------------
 
 def _decode(inp, start_pos):
