@@ -214,21 +214,31 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
     }
     const float moff = (m_ref == NEG_INF) ? 0.f : -m_ref * SCALE_LOG2;
-    float lsum = 0.f;
+    // The row sum adds the bf16 probabilities the P·V MFMA uses, two per dot2
+    // instruction against (1, 1): half the VALU work of fp32 adds, and the
+    // numerator and denominator then weight the same rounded values.
+    const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+    float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        float p[8];
+        bf16x2 pb[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + e], SCALE_LOG2, moff));
-          lsum += p[e];
+        for (int e = 0; e < 4; ++e) {
+          const f32x2 pp = {
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e], SCALE_LOG2, moff)),
+              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e + 1], SCALE_LOG2, moff))};
+          pb[e] = __builtin_convertvector(pp, bf16x2);
         }
-        pf[kb2 * 2 + hf] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                 pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pb[0], ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pb[1], ones, ls1, false);
+        ls0 = __builtin_amdgcn_fdot2_f32_bf16(pb[2], ones, ls0, false);
+        ls1 = __builtin_amdgcn_fdot2_f32_bf16(pb[3], ones, ls1, false);
+        pf[kb2 * 2 + hf] = u32x4{__builtin_bit_cast(uint32_t, pb[0]), __builtin_bit_cast(uint32_t, pb[1]),
+                                 __builtin_bit_cast(uint32_t, pb[2]), __builtin_bit_cast(uint32_t, pb[3])};
       }
-    l_run += lsum;
+    l_run += ls0 + ls1;
   };
 
   // O^T[d][q] += V^T[d][keys] · P^T[keys][q] for tile t; group sg holds keys
