@@ -10,7 +10,9 @@ attention" page, parameter table and in/out header):
   * weights W_Q [4096,4096], W_K [1024,4096], W_V [1024,4096], W_O [4096,4096],
     stored [out, in] as the "Query projection" page notes; N(0, 0.02^2);
   * block input x [B, T, 4096] ~ N(0, 1);
-  * decode K/V cache [B, S_max, 8, 128] ~ N(0, 1).
+  * decode K/V cache [B, S_max, 8, 128] ~ N(0, 1);
+  * gain of the pre-attention RMS normalisation [4096] ~ 1 + N(0, 0.2^2), from
+    a stream of its own (make_norm_weight).
 Each value is drawn as a float32 standard normal from numpy's PCG64 generator,
 scaled by the standard deviation in float32 and rounded to bf16 with
 round-to-nearest-even. Generation order: W_Q, W_K, W_V, W_O, x, cache K,
@@ -89,6 +91,16 @@ def make_block_inputs(seed: int, B: int, T: int, *, d: int = D_MODEL,
         kc = normal_bf16(rng, (B, cache_len, n_kv, d_head), cache_std)
         vc = normal_bf16(rng, (B, cache_len, n_kv, d_head), cache_std)
     return BlockInputs(x=x, wq=wq, wk=wk, wv=wv, wo=wo, k_cache=kc, v_cache=vc)
+
+
+def make_norm_weight(seed: int, d: int = D_MODEL, std: float = 0.2) -> np.ndarray:
+    """Gain of the pre-attention RMS normalisation: bf16 bits of 1 + N(0, std^2)
+    per feature (float32, rounded to nearest even). A trained gain is not all
+    ones; the spread makes a gain applied to the wrong feature visible. Drawn
+    from its own stream so that the block inputs of a seed are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    v = np.float32(1.0) + rng.standard_normal(d, dtype=np.float32) * np.float32(std)
+    return f32_to_bf16_bits(v)
 
 
 def sample_positions(seed: int, T: int, per_group: int = 64, n_groups: int = N_KV_HEADS,

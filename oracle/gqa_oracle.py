@@ -40,6 +40,7 @@ from typing import Optional
 import numpy as np
 
 ROPE_THETA = 500000.0
+NORM_EPS = 1e-5     # norm_eps of the Llama 3 / 3.1 8B catalogue entries
 
 
 # --- dtype -------------------------------------------------------------------
@@ -50,6 +51,12 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     if b.dtype != np.uint16:
         raise TypeError("expected uint16 bf16 bit patterns")
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _f64(a) -> np.ndarray:
+    """bf16 bit patterns (uint16) or any float array -> float64."""
+    a = np.asarray(a)
+    return bf16_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
 # --- steps 1-3: projections ----------------------------------------------------
@@ -295,6 +302,55 @@ def block_forward_rows(x, wq, wk, wv, wo, n_heads: int, n_kv: int, rows,
                 h[r0:r1, hd] = softmax_rows(s) @ vg
     hm = h.reshape(len(rows), n_heads * dh)
     return dict(rows=rows, h=hm, delta=project(hm, wo))
+
+
+# --- the block's handoff: pre-norm and residual --------------------------------------
+#
+# The "Llama 3.1 8B · Merge and project" page, section "Contextual evidence from
+# Output projection" (the model.py handoff excerpt), feeds the attention the
+# normalised input attention_norm(x) and adds its update to x itself. The module
+# there is RMSNorm(dim, eps=norm_eps) with norm_eps = 1e-5 (catalogue entry), but
+# no page writes its formula out. Reading taken: root-mean-square layer
+# normalisation (Zhang & Sennrich, 2019) with a learned per-feature gain and eps
+# added under the root; evaluated exactly here (the pages' own code rounds twice,
+# after the scaling and after the gain; this oracle rounds nothing).
+
+def rms_norm(x, weight, eps: float = NORM_EPS) -> np.ndarray:
+    """y[..., i] = weight[i] · x[..., i] / sqrt(mean over j of x[..., j]^2 + eps), fp64.
+
+    Merge and project page, handoff excerpt (attention_norm), with the
+    definition stated above.
+    """
+    x = _f64(x)
+    w = _f64(weight)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * w
+
+
+def prenorm_block_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, *,
+                          eps: float = NORM_EPS, **kw) -> dict:
+    """out = x + Δ_attn(rms_norm(x)): the attention half of the block with its
+    handoff (Merge and project page, handoff excerpt). Keyword arguments go to
+    block_forward (causal, mask, start_pos, caches). Returns block_forward's
+    intermediates plus x_norm and out."""
+    x = _f64(x)
+    xn = rms_norm(x, norm_w, eps)
+    r = block_forward(xn, wq, wk, wv, wo, n_heads, n_kv, **kw)
+    r["x_norm"] = xn
+    r["out"] = x + r["delta"]
+    return r
+
+
+def prenorm_decode_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, k_cache,
+                           v_cache, start_pos: int, eps: float = NORM_EPS,
+                           theta: float = ROPE_THETA) -> dict:
+    """decode_forward on rms_norm(x) plus the residual: out = x + Δ, x [B, d]."""
+    x = _f64(x)
+    xn = rms_norm(x, norm_w, eps)
+    r = decode_forward(xn, wq, wk, wv, wo, n_heads, n_kv, k_cache, v_cache, start_pos, theta)
+    r["x_norm"] = xn
+    r["out"] = x + r["delta"]
+    return r
 
 
 def param_counts(d: int, n_heads: int, n_kv: int) -> dict:

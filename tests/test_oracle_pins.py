@@ -297,3 +297,75 @@ def test_sampled_rows_match_full_oracle():
         r = O.block_forward_rows(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8, rows, batch_index=b)
         assert np.allclose(r["delta"], full["delta"][b, rows], rtol=1e-12, atol=1e-12)
         assert np.allclose(r["h"], full["h"][b, rows], rtol=1e-12, atol=1e-12)
+
+
+# --- pre-norm and residual (the block's handoff) ------------------------------------
+
+def test_rms_norm_one_hot_closed_form():
+    # x = a·e_k in n features: mean square a²/n, so with eps = 0 the output is
+    # sign(a)·sqrt(n)·w_k at feature k and zero elsewhere. A sum in place of the
+    # mean, a missing root or a gain taken from another feature all fail here.
+    n = 16
+    w = 1.0 + np.arange(n) / 8.0
+    for k, a in ((0, 3.0), (5, -0.25), (15, 1e-3)):
+        x = np.zeros(n)
+        x[k] = a
+        y = O.rms_norm(x, w, eps=0.0)
+        want = np.zeros(n)
+        want[k] = math.copysign(math.sqrt(n), a) * w[k]
+        assert np.allclose(y, want, rtol=1e-14, atol=0)
+
+
+def test_rms_norm_eps_sits_under_the_root():
+    # a constant row c: y = w·c/sqrt(c² + eps). At c = 1e-3 and eps = 1e-5 that is
+    # 1e-3/sqrt(1.1e-5) = 0.30151..., far from c/(|c| + eps) = 0.990 or
+    # c/sqrt(c²) = 1 (eps added outside the root, or dropped).
+    c, eps = 1e-3, 1e-5
+    y = O.rms_norm(np.full((2, 8), c), np.ones(8), eps=eps)
+    assert np.allclose(y, 0.30151134457776363, rtol=1e-12)
+    assert O.NORM_EPS == 1e-5
+
+
+def test_rms_norm_unit_mean_square_and_scale_invariance():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 5, 64)) * 7.0
+    y = O.rms_norm(x, np.ones(64), eps=0.0)
+    assert np.allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-13)
+    assert np.all(np.sign(y) == np.sign(x))          # a positive rescaling per row
+    assert np.allclose(O.rms_norm(x * 0.01, np.ones(64), eps=0.0), y, rtol=1e-12)
+    # rows are normalised independently
+    assert np.allclose(O.rms_norm(x[1:2], np.ones(64), eps=0.0), y[1:2], rtol=1e-13)
+
+
+def test_prenorm_zero_gain_leaves_the_input():
+    # gain 0: the normalised input is 0, so Q = K = V = 0, every head averages zero
+    # values and Δ = 0: the residual must give back x exactly (not x̂, not Δ alone).
+    x, wq, wk, wv, wo, _, _ = _tiny(21, B=2, T=5)
+    r = O.prenorm_block_forward(x, np.zeros(16), wq, wk, wv, wo, 4, 2)
+    assert np.array_equal(r["out"], x)
+    assert np.array_equal(r["delta"], np.zeros_like(x))
+
+
+def test_prenorm_residual_adds_x_to_the_normalised_block():
+    # out − x is the block applied to the normalised rows; scaling x by α > 0
+    # leaves that part unchanged (eps = 0), so out(αx) − αx = out(x) − x.
+    x, wq, wk, wv, wo, kc, vc = _tiny(22, B=1, T=6)
+    g = 1.0 + np.random.default_rng(5).standard_normal(16) * 0.3
+    r1 = O.prenorm_block_forward(x, g, wq, wk, wv, wo, 4, 2, eps=0.0)
+    r2 = O.prenorm_block_forward(3.5 * x, g, wq, wk, wv, wo, 4, 2, eps=0.0)
+    assert np.allclose(r2["out"] - 3.5 * x, r1["out"] - x, rtol=1e-10, atol=1e-12)
+    assert not np.allclose(r1["out"] - x, O.block_forward(x, wq, wk, wv, wo, 4, 2)["delta"])
+    # decode form: same block at one position over the cache
+    x, wq, wk, wv, wo, kc, vc = _tiny(23, B=2, T=1, cache=4)
+    d = O.prenorm_decode_forward(x[:, 0], g, wq, wk, wv, wo, 4, 2, kc, vc, 3)
+    p = O.prenorm_block_forward(x, g, wq, wk, wv, wo, 4, 2, start_pos=3, k_cache=kc,
+                                v_cache=vc)
+    assert np.allclose(d["out"], p["out"][:, 0], rtol=1e-12, atol=1e-14)
+
+
+def test_norm_gain_generator_is_seeded_and_centred():
+    g1, g2 = gi.make_norm_weight(3), gi.make_norm_weight(3)
+    assert g1.dtype == np.uint16 and g1.shape == (4096,) and np.array_equal(g1, g2)
+    v = O.bf16_to_f64(g1)
+    assert abs(v.mean() - 1.0) < 0.02 and 0.17 < v.std() < 0.23
+    assert not np.array_equal(g1, gi.make_norm_weight(4))
