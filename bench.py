@@ -6,8 +6,9 @@ with rotation, grouped flash attention, output projection) per step, in
 TFLOP/s of algorithmic work (only unmasked query/key pairs count). Also
 measured in the same run: decode (B=64, one token at position 8191 over a
 bf16 KV cache of 8192 rows) in HBM GB/s, chunked prefill (B=1, 2048 new
-positions after 2048 cached ones), and prefill at B=8, T=4096 and at
-B=1, T=131072.
+positions after 2048 cached ones), the pre-norm + residual forms of the
+headline prefill and of decode, and prefill at B=8, T=4096 and at B=1,
+T=131072.
 
 Prints one JSON line. Inputs are seeded synthetic bf16 values resident in HBM
 before the timed region. `roofline` describes the kernel that takes the most
@@ -16,7 +17,7 @@ time in the headline step, timed with HIP events on the stream it runs on;
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-       python bench.py --only decode|chunk|prefill_B8_T4096|prefill_B1_T131072
+       python bench.py --only decode|chunk|prenorm|prefill_B8_T4096|prefill_B1_T131072
 """
 
 import argparse
@@ -274,6 +275,65 @@ class Bench:
         del kc, vc, ws
         torch.cuda.empty_cache()
 
+    # ---------------- pre-norm + residual forms (the block's handoff) ----------------
+    def prenorm(self, extra):
+        """out = x + Δ(RMSNorm(x)) at the headline prefill shape and the decode shape;
+        the normalisation kernel's own time and bandwidth at the prefill shape."""
+        torch, gqa, args = self.torch, self.gqa, self.args
+        B, T = 1, 2048
+        self.log("[bench] pre-norm + residual: prefill B=1 T=2048")
+        inp = self.gi.make_block_inputs(2, B, T)
+        g = self.up(self.gi.make_norm_weight(2))
+        x = self.up(inp.x)
+        w = [self.up(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo)]
+        rope = torch.from_numpy(gqa.rope_table(np.arange(T))).to(self.dev)
+        out = torch.empty((B, T, 4096), dtype=torch.float32, device=self.dev)
+        ws = torch.empty(gqa.prefill_workspace_bytes(B, T), dtype=torch.uint8, device=self.dev)
+        plain = lambda: gqa.block_forward(x, *w, rope, causal=True, out=out, workspace=ws)
+        pre = lambda: gqa.block_forward(x, *w, rope, causal=True, out=out, workspace=ws,
+                                        norm_w=g)
+        ms_plain, _ = self.time_steps(plain, args.steps, args.warmup)
+        ms_pre, _ = self.time_steps(pre, args.steps, args.warmup)
+        y = torch.empty_like(x)
+        ms_norm, _ = self.time_steps(lambda: gqa.rmsnorm(x, g, y=y), args.steps, args.warmup)
+        F = prefill_flops(B, T)
+        nb = 2 * B * T * 4096 * 2
+        extra["prenorm_prefill_B1_T2048"] = {
+            "ms": round(ms_pre, 5), "TFLOP/s": round(F / (ms_pre * 1e-3) / 1e12, 1),
+            "plain_block_ms": round(ms_plain, 5),
+            "overhead_frac": round(ms_pre / ms_plain - 1.0, 4),
+            "rmsnorm_kernel": {"ms": round(ms_norm, 5),
+                               "GB/s": round(nb / (ms_norm * 1e-3) / 1e9, 1),
+                               "bytes": nb}}
+        self.log(f"[bench] pre-norm prefill: {ms_pre:.4f} ms vs plain {ms_plain:.4f} ms; "
+                 f"rmsnorm {ms_norm * 1e3:.1f} us")
+        del x, w, out, ws, y
+
+        Bd, S, sp = 64, 8192, 8191
+        self.log("[bench] pre-norm + residual: decode B=64 kv=8192")
+        dinp = self.gi.make_block_inputs(4, Bd, 1, cache_len=S)
+        dg = self.up(self.gi.make_norm_weight(4))
+        dx = self.up(dinp.x[:, 0])
+        dw = [self.up(a) for a in (dinp.wq, dinp.wk, dinp.wv, dinp.wo)]
+        kc, vc = self.up(dinp.k_cache), self.up(dinp.v_cache)
+        del dinp
+        drope = torch.from_numpy(gqa.rope_table([sp])[0]).to(self.dev)
+        dout = torch.empty((Bd, 4096), dtype=torch.float32, device=self.dev)
+        dws = torch.empty(gqa.decode_workspace_bytes(Bd, S), dtype=torch.uint8, device=self.dev)
+        dplain = lambda: gqa.decode_forward(dx, *dw, drope, kc, vc, sp, out=dout, workspace=dws)
+        dpre = lambda: gqa.decode_forward(dx, *dw, drope, kc, vc, sp, out=dout, workspace=dws,
+                                          norm_w=dg)
+        dms_plain, _ = self.time_steps(dplain, args.steps, args.warmup)
+        dms, _ = self.time_steps(dpre, args.steps, args.warmup)
+        nbytes = decode_bytes(Bd, S) + 4096 * 2   # plus the gain
+        extra["prenorm_decode_B64_kv8192"] = {
+            "ms": round(dms, 5), "GB/s": round(nbytes / (dms * 1e-3) / 1e9, 1),
+            "plain_decode_ms": round(dms_plain, 5),
+            "overhead_frac": round(dms / dms_plain - 1.0, 4)}
+        self.log(f"[bench] pre-norm decode: {dms:.4f} ms vs plain {dms_plain:.4f} ms")
+        del kc, vc, dws
+        torch.cuda.empty_cache()
+
     def prefill_b8(self, extra):
         self.prefill(extra, 8, 4096, 3, max(3, self.args.steps // 4))
 
@@ -322,7 +382,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--only", choices=["decode", "chunk", "prefill_B8_T4096",
+    ap.add_argument("--only", choices=["decode", "chunk", "prenorm", "prefill_B8_T4096",
                                        "prefill_B1_T131072"],
                     help="run just this one workload and print its figures (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -338,7 +398,8 @@ def main():
     if args.calibrate_copy:
         b.calibrate_copy(args.calibrate_copy)
         return
-    others = {"decode": b.decode, "chunk": b.chunk, "prefill_B8_T4096": b.prefill_b8,
+    others = {"decode": b.decode, "chunk": b.chunk, "prenorm": b.prenorm,
+              "prefill_B8_T4096": b.prefill_b8,
               "prefill_B1_T131072": b.prefill_long}
     if args.only:
         extra = {}

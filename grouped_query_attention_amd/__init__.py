@@ -6,9 +6,9 @@ passed to the C ABI as raw pointers. There is no fallback: if libgqa.so is
 missing or cannot be loaded, every call raises.
 
 Names follow include/gqa.h:
-    block_forward, decode_forward, qkv_rope, attention, output_projection,
-    decode_attention, rope_table, prefill_workspace_bytes,
-    decode_workspace_bytes, dims.
+    block_forward, chunk_forward, decode_forward (each with a pre-norm and
+    residual form: norm_w=... ), qkv_rope, attention, output_projection,
+    decode_attention, rmsnorm, rope_table, the *_workspace_bytes sizes, dims.
 """
 
 from __future__ import annotations
@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 D_MODEL, N_HEADS, N_KV_HEADS, D_HEAD, N_PAIRS = 4096, 32, 8, 128, 64
 ROPE_THETA = 500000.0
+NORM_EPS = 1e-5
 
 _lib = None
 
@@ -46,6 +47,7 @@ def _load():
                            "`python -m grouped_query_attention_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, Z, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    F = ctypes.c_float
     sig = {
         "gqa_status_string": (ctypes.c_char_p, [I]),
         "gqa_dims": (None, [P, P, P, P]),
@@ -61,6 +63,13 @@ def _load():
         "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P, Z, P]),
         "gqa_output_projection": (I, [P, P, I, P, P]),
         "gqa_decode_attention": (I, [P, P, P, I, I, I, P, P, Z, P]),
+        "gqa_block_forward_prenorm": (I, [P, P, F, P, P, P, P, P, P, I, I, I, I, P, P, P, Z,
+                                          P]),
+        "gqa_chunk_forward_prenorm": (I, [P, P, F, P, P, P, P, P, P, P, I, I, I, I, P, P, P,
+                                          Z, P]),
+        "gqa_decode_forward_prenorm": (I, [P, P, F, P, P, P, P, P, P, P, I, I, I, P, P, P, Z,
+                                           P]),
+        "gqa_rmsnorm": (I, [P, P, F, I, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -80,7 +89,9 @@ def exported_symbols():
             "gqa_decode_workspace_bytes", "gqa_attention_workspace_bytes",
             "gqa_chunk_workspace_bytes", "gqa_block_forward", "gqa_chunk_forward",
             "gqa_decode_forward",
-            "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention"]
+            "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention",
+            "gqa_block_forward_prenorm", "gqa_chunk_forward_prenorm",
+            "gqa_decode_forward_prenorm", "gqa_rmsnorm"]
 
 
 # --- helpers -------------------------------------------------------------------------
@@ -153,8 +164,12 @@ def attention_workspace_bytes(B: int, T: int, kv_len: int, causal: bool = True) 
 # --- device entries -------------------------------------------------------------------
 
 def block_forward(x, w_q, w_k, w_v, w_o, rope, *, causal: bool = True, mask=None,
-                  out=None, h_out=None, workspace=None, stream=None):
-    """Δ = GQA block forward for x [B, T, 4096] bf16; returns out [B, T, 4096] fp32."""
+                  out=None, h_out=None, workspace=None, norm_w=None, eps: float = NORM_EPS,
+                  stream=None):
+    """Δ = GQA block forward for x [B, T, 4096] bf16; returns out [B, T, 4096] fp32.
+
+    With norm_w ([4096] bf16 gain) the block reads RMSNorm(x) and returns x + Δ.
+    """
     import torch
     B, T, _ = x.shape
     _req(x, torch.bfloat16, (B, T, D_MODEL), "x")
@@ -169,19 +184,25 @@ def block_forward(x, w_q, w_k, w_v, w_o, rope, *, causal: bool = True, mask=None
     need = prefill_workspace_bytes(B, T)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    st = _load().gqa_block_forward(
-        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(mask),
-        int(bool(causal)), B, T, T, _ptr(out), _ptr(h_out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("gqa_block_forward", st)
+    args = (_ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(mask),
+            int(bool(causal)), B, T, T, _ptr(out), _ptr(h_out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if norm_w is None:
+        _check("gqa_block_forward", _load().gqa_block_forward(_ptr(x), *args))
+    else:
+        _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
+        _check("gqa_block_forward_prenorm",
+               _load().gqa_block_forward_prenorm(_ptr(x), _ptr(norm_w), float(eps), *args))
     return out
 
 
 def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,
-                   out=None, h_out=None, workspace=None, stream=None):
+                   out=None, h_out=None, workspace=None, norm_w=None, eps: float = NORM_EPS,
+                   stream=None):
     """One new position per sequence at start_pos; x [B, 4096]; returns out [B, 4096] fp32.
 
-    Writes the new rotated key and value into cache slot start_pos.
+    Writes the new rotated key and value into cache slot start_pos. With norm_w
+    the block reads RMSNorm(x) and returns x + Δ.
     """
     import torch
     B = x.shape[0]
@@ -195,20 +216,26 @@ def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int
     if workspace is None:
         workspace = torch.empty(decode_workspace_bytes(B, S_max), dtype=torch.uint8,
                                 device=x.device)
-    st = _load().gqa_decode_forward(
-        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
-        _ptr(v_cache), B, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("gqa_decode_forward", st)
+    args = (_ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
+            _ptr(v_cache), B, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if norm_w is None:
+        _check("gqa_decode_forward", _load().gqa_decode_forward(_ptr(x), *args))
+    else:
+        _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
+        _check("gqa_decode_forward_prenorm",
+               _load().gqa_decode_forward_prenorm(_ptr(x), _ptr(norm_w), float(eps), *args))
     return out
 
 
 def chunk_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,
-                  out=None, h_out=None, workspace=None, stream=None):
+                  out=None, h_out=None, workspace=None, norm_w=None, eps: float = NORM_EPS,
+                  stream=None):
     """T new positions per sequence at start_pos .. start_pos+T-1 over a KV cache
     holding positions 0 .. start_pos-1; x [B, T, 4096]; returns out [B, T, 4096] fp32.
 
     Writes the new rotated keys and values into cache slots start_pos .. start_pos+T-1.
+    With norm_w the block reads RMSNorm(x) and returns x + Δ.
     """
     import torch
     B, T, _ = x.shape
@@ -222,12 +249,32 @@ def chunk_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int,
     if workspace is None:
         workspace = torch.empty(chunk_workspace_bytes(B, T, start_pos), dtype=torch.uint8,
                                 device=x.device)
-    st = _load().gqa_chunk_forward(
-        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
-        _ptr(v_cache), B, T, S_max, int(start_pos), _ptr(out), _ptr(h_out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream))
-    _check("gqa_chunk_forward", st)
+    args = (_ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
+            _ptr(v_cache), B, T, S_max, int(start_pos), _ptr(out), _ptr(h_out),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if norm_w is None:
+        _check("gqa_chunk_forward", _load().gqa_chunk_forward(_ptr(x), *args))
+    else:
+        _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
+        _check("gqa_chunk_forward_prenorm",
+               _load().gqa_chunk_forward_prenorm(_ptr(x), _ptr(norm_w), float(eps), *args))
     return out
+
+
+def rmsnorm(x, norm_w, eps: float = NORM_EPS, *, y=None, stream=None):
+    """y = RMSNorm(x) (bf16, same shape) for x [..., 4096] bf16 and gain norm_w [4096]."""
+    import torch
+    _req(x, torch.bfloat16, None, "x")
+    _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
+    if x.shape[-1] != D_MODEL:
+        raise ValueError(f"x: last dimension must be {D_MODEL}")
+    M = x.numel() // D_MODEL
+    if y is None:
+        y = torch.empty_like(x)
+    _req(y, torch.bfloat16, tuple(x.shape), "y")
+    _check("gqa_rmsnorm", _load().gqa_rmsnorm(_ptr(x), _ptr(norm_w), float(eps), M, _ptr(y),
+                                              _stream(stream)))
+    return y
 
 
 def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None):

@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgqa.so")
 
-SOURCES = ["gqa_api.hip", "gemm.hip", "attention.hip"]
+SOURCES = ["gqa_api.hip", "gemm.hip", "attention.hip", "norm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -54,6 +54,8 @@ struct GemmArgs {
   uint16_t* k_dst; uint16_t* v_dst; long long kv_bstride, kv_rstride;
   // fp32 epilogue: out[M][N]; split-K partials: out + blockIdx.y*M*N
   float* out;
+  // fp32 epilogue: optional bf16 residual [M][N] added to the product (null: none)
+  const uint16_t* resid;
 };
 
 // Chunk permutation of row r for LDS rows of KB bf16 (KB/8 chunks of 16 bytes).
@@ -273,9 +275,16 @@ void gemm_nt_kernel(GemmArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int tok = m0 + wp * C::WP + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
         if (tok >= a.M) continue;
-        float* orow = obase + (size_t)tok * a.N + n0 + wq * C::WQ + lrow;
+        const size_t off = (size_t)tok * a.N + n0 + wq * C::WQ + lrow;
+        float* orow = obase + off;
+        if (EPI == EPI_OUT_F32 && a.resid) {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j) orow[j * 32] = acc[i][j][r];
+          for (int j = 0; j < NQ; ++j)
+            orow[j * 32] = acc[i][j][r] + __builtin_bit_cast(float, (uint32_t)a.resid[off + j * 32] << 16);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NQ; ++j) orow[j * 32] = acc[i][j][r];
+        }
       }
     }
   }
@@ -324,7 +333,8 @@ __global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a) {
   *reinterpret_cast<u32x2*>(dst) = w;
 }
 
-// Split-K epilogue of the output projection: out[M][4096] = sum of partials.
+// Split-K epilogue of the output projection: out[M][4096] = sum of partials
+// (+ the bf16 residual when a.resid is set).
 template <int KS>
 __global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, float* out) {
   constexpr int PER_TOK = D_MODEL / 4;
@@ -332,7 +342,13 @@ __global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, float* out)
   if (idx >= a.M * PER_TOK) return;
   const int tok = idx / PER_TOK;
   const int col = (idx - tok * PER_TOK) * 4;
-  *reinterpret_cast<f32x4*>(out + (size_t)tok * D_MODEL + col) = sum_partials<KS>(a, tok, col);
+  const size_t off = (size_t)tok * D_MODEL + col;
+  f32x4 v = sum_partials<KS>(a, tok, col);
+  if (a.resid) {
+    const u32x2 x = *reinterpret_cast<const u32x2*>(a.resid + off);
+    v += f32x4{bf16lo(x[0]), bf16hi(x[0]), bf16lo(x[1]), bf16hi(x[1])};
+  }
+  *reinterpret_cast<f32x4*>(out + off) = v;
 }
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
@@ -392,9 +408,9 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
 }
 
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
-                           float* splitk, hipStream_t s) {
+                           const uint16_t* resid, float* splitk, hipStream_t s) {
   GemmArgs a{};
-  a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1;
+  a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1; a.resid = resid;
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);

@@ -90,6 +90,154 @@ int check_weights(const gqa_bf16* wq, const gqa_bf16* wk, const gqa_bf16* wv,
   return GQA_OK;
 }
 
+// Pre-attention RMS normalisation and residual of the *_prenorm entries; a
+// null gain means the plain block (no normalisation, out = Δ).
+struct PreNorm {
+  const gqa_bf16* gain;
+  float eps;
+};
+
+int check_prenorm(const PreNorm& n) {
+  if (!n.gain) return GQA_ERR_NULL;
+  if (!(n.eps >= 0.f) || !std::isfinite(n.eps)) return GQA_ERR_ARG;
+  if (misaligned(n.gain)) return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+// With a gain: x̂ = RMSNorm(x) into `xn` (a workspace region the attention
+// output overwrites later on the same stream) and the projections read x̂.
+const gqa_bf16* norm_input(const PreNorm* n, const gqa_bf16* x, int M, gqa_bf16* xn,
+                           hipStream_t s, hipError_t* e) {
+  *e = hipSuccess;
+  if (!n) return x;
+  *e = gqa::launch_rmsnorm(x, n->gain, n->eps, M, xn, s);
+  return xn;
+}
+
+int block_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
+               const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
+               const float* rope, const float* mask, int causal, int B, int T, int kv_len,
+               float* out, gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (!x || !rope || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st == GQA_OK && norm) st = check_prenorm(*norm);
+  if (st != GQA_OK) return st;
+  if (causal != 0 && causal != 1) return GQA_ERR_ARG;
+  if (causal && mask) return GQA_ERR_ARG;
+  if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
+  if (kv_len != T) return GQA_ERR_UNSUPPORTED;
+  if (misaligned(x) || misaligned(rope) || misaligned(out) || (mask && misaligned(mask)) ||
+      (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const long long M = (long long)B * T;
+  const PrefillWs L = prefill_layout(B, T);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  auto* k = reinterpret_cast<gqa_bf16*>(ws + L.k);
+  auto* v = reinterpret_cast<gqa_bf16*>(ws + L.v);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+
+  hipError_t e;
+  const gqa_bf16* xin =
+      norm_input(norm, x, (int)M, reinterpret_cast<gqa_bf16*>(ws + L.h), s, &e);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_qkv_rope(xin, w_q, w_k, w_v, rope, (int)M, T, q,
+                           (long long)T * D_MODEL, D_MODEL, k, v,
+                           (long long)T * KV_W, KV_W, part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
+                                  h, part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, norm ? x : nullptr, part, s));
+}
+
+int chunk_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
+               const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
+               const float* rope, gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int T,
+               int S_max, int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st == GQA_OK && norm) st = check_prenorm(*norm);
+  if (st != GQA_OK) return st;
+  if (!tokens_ok(B, T) || S_max < 1 || start_pos < 0 || (long long)start_pos + T > S_max)
+    return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
+      misaligned(out) || (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const ChunkWs L = chunk_layout(B, T, start_pos);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  const long long M = (long long)B * T;
+  const long long cache_bstride = (long long)S_max * KV_W;
+
+  hipError_t e;
+  const gqa_bf16* xin =
+      norm_input(norm, x, (int)M, reinterpret_cast<gqa_bf16*>(ws + L.h), s, &e);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  // new keys and values go straight into cache slots start_pos .. start_pos+T-1
+  e = gqa::launch_qkv_rope(xin, w_q, w_k, w_v, rope, (int)M, T, q,
+                           (long long)T * D_MODEL, D_MODEL,
+                           k_cache + (size_t)start_pos * KV_W,
+                           v_cache + (size_t)start_pos * KV_W, cache_bstride, KV_W,
+                           part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_flash_attention(q, k_cache, v_cache, cache_bstride, nullptr, 1, B, T,
+                                  start_pos + T, start_pos, h, part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, norm ? x : nullptr, part, s));
+}
+
+int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
+                const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
+                const float* rope, gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
+                int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
+  int st = check_weights(w_q, w_k, w_v, w_o);
+  if (st == GQA_OK && norm) st = check_prenorm(*norm);
+  if (st != GQA_OK) return st;
+  if (B < 1 || B > GQA_MAX_TOKENS || S_max < 1 || start_pos < 0 || start_pos >= S_max)
+    return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
+      misaligned(out) || (h_out && misaligned(h_out)))
+    return GQA_ERR_ALIGN;
+  const DecodeWs L = decode_layout(B, S_max);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
+  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  hipStream_t s = (hipStream_t)stream;
+  const long long cache_bstride = (long long)S_max * KV_W;
+
+  hipError_t e;
+  const gqa_bf16* xin = norm_input(norm, x, B, reinterpret_cast<gqa_bf16*>(ws + L.h), s, &e);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_qkv_rope(xin, w_q, w_k, w_v, rope, B, 1, q, D_MODEL, 0,
+                           k_cache + (size_t)start_pos * KV_W,
+                           v_cache + (size_t)start_pos * KV_W, cache_bstride, 0,
+                           part, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_out_proj(h, w_o, B, out, norm ? x : nullptr, part, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -192,83 +340,7 @@ int gqa_output_projection(const gqa_bf16* h, const gqa_bf16* w_o, int M, float* 
   if (!h || !w_o || !out) return GQA_ERR_NULL;
   if (M < 1 || M > GQA_MAX_TOKENS) return GQA_ERR_SHAPE;
   if (misaligned(h) || misaligned(w_o) || misaligned(out)) return GQA_ERR_ALIGN;
-  return hip_status(gqa::launch_out_proj(h, w_o, M, out, nullptr, (hipStream_t)stream));
-}
-
-int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
-                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
-                      const float* mask, int causal, int B, int T, int kv_len, float* out,
-                      gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
-                      void* stream) {
-  if (!x || !rope || !out) return GQA_ERR_NULL;
-  int st = check_weights(w_q, w_k, w_v, w_o);
-  if (st != GQA_OK) return st;
-  if (causal != 0 && causal != 1) return GQA_ERR_ARG;
-  if (causal && mask) return GQA_ERR_ARG;
-  if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
-  if (kv_len != T) return GQA_ERR_UNSUPPORTED;
-  if (misaligned(x) || misaligned(rope) || misaligned(out) || (mask && misaligned(mask)) ||
-      (h_out && misaligned(h_out)))
-    return GQA_ERR_ALIGN;
-  const long long M = (long long)B * T;
-  const PrefillWs L = prefill_layout(B, T);
-  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
-  if (misaligned(workspace)) return GQA_ERR_ALIGN;
-
-  char* ws = static_cast<char*>(workspace);
-  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
-  auto* k = reinterpret_cast<gqa_bf16*>(ws + L.k);
-  auto* v = reinterpret_cast<gqa_bf16*>(ws + L.v);
-  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
-  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
-  hipStream_t s = (hipStream_t)stream;
-
-  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
-                                      (long long)T * D_MODEL, D_MODEL, k, v,
-                                      (long long)T * KV_W, KV_W, part, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
-                                  h, part, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, part, s));
-}
-
-int gqa_chunk_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
-                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
-                      gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int T, int S_max,
-                      int start_pos, float* out, gqa_bf16* h_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
-  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
-  int st = check_weights(w_q, w_k, w_v, w_o);
-  if (st != GQA_OK) return st;
-  if (!tokens_ok(B, T) || S_max < 1 || start_pos < 0 || (long long)start_pos + T > S_max)
-    return GQA_ERR_SHAPE;
-  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
-      misaligned(out) || (h_out && misaligned(h_out)))
-    return GQA_ERR_ALIGN;
-  const ChunkWs L = chunk_layout(B, T, start_pos);
-  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
-  if (misaligned(workspace)) return GQA_ERR_ALIGN;
-
-  char* ws = static_cast<char*>(workspace);
-  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
-  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
-  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
-  hipStream_t s = (hipStream_t)stream;
-  const long long M = (long long)B * T;
-  const long long cache_bstride = (long long)S_max * KV_W;
-
-  // new keys and values go straight into cache slots start_pos .. start_pos+T-1
-  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q,
-                                      (long long)T * D_MODEL, D_MODEL,
-                                      k_cache + (size_t)start_pos * KV_W,
-                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, KV_W,
-                                      part, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  e = gqa::launch_flash_attention(q, k_cache, v_cache, cache_bstride, nullptr, 1, B, T,
-                                  start_pos + T, start_pos, h, part, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, part, s));
+  return hip_status(gqa::launch_out_proj(h, w_o, M, out, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int gqa_decode_attention(const gqa_bf16* q_r, const gqa_bf16* k_cache,
@@ -288,38 +360,75 @@ int gqa_decode_attention(const gqa_bf16* q_r, const gqa_bf16* k_cache,
                                                  h_out, (hipStream_t)stream));
 }
 
+int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                      const float* mask, int causal, int B, int T, int kv_len, float* out,
+                      gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return block_impl(x, nullptr, w_q, w_k, w_v, w_o, rope, mask, causal, B, T, kv_len, out,
+                    h_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_block_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                              const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                              const gqa_bf16* w_o, const float* rope, const float* mask,
+                              int causal, int B, int T, int kv_len, float* out,
+                              gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const PreNorm n{norm_w, eps};
+  return block_impl(x, &n, w_q, w_k, w_v, w_o, rope, mask, causal, B, T, kv_len, out, h_out,
+                    workspace, workspace_bytes, stream);
+}
+
+int gqa_chunk_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                      const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                      gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int T, int S_max,
+                      int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return chunk_impl(x, nullptr, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, T, S_max,
+                    start_pos, out, h_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_chunk_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                              const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                              const gqa_bf16* w_o, const float* rope, gqa_bf16* k_cache,
+                              gqa_bf16* v_cache, int B, int T, int S_max, int start_pos,
+                              float* out, gqa_bf16* h_out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  const PreNorm n{norm_w, eps};
+  return chunk_impl(x, &n, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, T, S_max, start_pos,
+                    out, h_out, workspace, workspace_bytes, stream);
+}
+
 int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                        const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
                        gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max, int start_pos,
                        float* out, gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
-  int st = check_weights(w_q, w_k, w_v, w_o);
+  return decode_impl(x, nullptr, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max,
+                     start_pos, out, h_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                               const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                               const gqa_bf16* w_o, const float* rope, gqa_bf16* k_cache,
+                               gqa_bf16* v_cache, int B, int S_max, int start_pos, float* out,
+                               gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  const PreNorm n{norm_w, eps};
+  return decode_impl(x, &n, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max, start_pos,
+                     out, h_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_rmsnorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, gqa_bf16* y,
+                void* stream) {
+  if (!x || !y) return GQA_ERR_NULL;
+  if (M < 1 || M > GQA_MAX_TOKENS) return GQA_ERR_SHAPE;
+  const PreNorm n{norm_w, eps};
+  const int st = check_prenorm(n);
   if (st != GQA_OK) return st;
-  if (B < 1 || B > GQA_MAX_TOKENS || S_max < 1 || start_pos < 0 || start_pos >= S_max)
-    return GQA_ERR_SHAPE;
-  if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
-      misaligned(out) || (h_out && misaligned(h_out)))
-    return GQA_ERR_ALIGN;
-  const DecodeWs L = decode_layout(B, S_max);
-  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
-  if (misaligned(workspace)) return GQA_ERR_ALIGN;
-
-  char* ws = static_cast<char*>(workspace);
-  auto* q = reinterpret_cast<gqa_bf16*>(ws + L.q);
-  gqa_bf16* h = h_out ? h_out : reinterpret_cast<gqa_bf16*>(ws + L.h);
-  float* part = reinterpret_cast<float*>(ws + L.part);
-  hipStream_t s = (hipStream_t)stream;
-  const long long cache_bstride = (long long)S_max * KV_W;
-
-  hipError_t e = gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, B, 1, q, D_MODEL, 0,
-                                      k_cache + (size_t)start_pos * KV_W,
-                                      v_cache + (size_t)start_pos * KV_W, cache_bstride, 0,
-                                      part, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
-  if (e != hipSuccess) return GQA_ERR_HIP;
-  return hip_status(gqa::launch_out_proj(h, w_o, B, out, part, s));
+  if (misaligned(x) || misaligned(y)) return GQA_ERR_ALIGN;
+  return hip_status(gqa::launch_rmsnorm(x, norm_w, eps, M, y, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -19,9 +19,14 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
                            long long kv_rstride, float* splitk, hipStream_t s);
 
-// out[M][4096] (fp32) = h[M][4096] · w_oᵀ; `splitk` as for launch_qkv_rope.
+// out[M][4096] (fp32) = h[M][4096] · w_oᵀ (+ resid[M][4096] bf16 when not null);
+// `splitk` as for launch_qkv_rope.
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
-                           float* splitk, hipStream_t s);
+                           const uint16_t* resid, float* splitk, hipStream_t s);
+
+// y[M][4096] (bf16) = RMS normalisation of x[M][4096] rows with gain w[4096].
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, int M, uint16_t* y,
+                          hipStream_t s);
 
 // Scratch bytes of the split-reduction path for M tokens (0 when M > 64).
 size_t gemm_splitk_bytes(int M);

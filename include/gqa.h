@@ -168,6 +168,50 @@ int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w
                        size_t workspace_bytes, void* stream);
 
 /*
+ * The attention half of the decoder block with its handoff ("Llama 3.1 8B ·
+ * Merge and project", section "Contextual evidence from Output projection",
+ * the model.py handoff excerpt): the block reads the RMS-normalised input and
+ * its update is added to the input,
+ *     x̂ = RMSNorm(x),  out = x + Δ(x̂),
+ *     RMSNorm(x)[t][i] = norm_w[i] · x[t][i] / sqrt(mean over j of x[t][j]^2 + eps)
+ * (the pages name RMSNorm and norm_eps = 1e-5 but not its formula; this is
+ * root-mean-square layer normalisation with eps under the root). x̂ is rounded
+ * to bf16 once before the projections; the residual adds the bf16 input x to
+ * the fp32 Δ. Each variant takes the arguments, workspace and errors of the
+ * entry point it extends, plus
+ *   norm_w  [4096]   bf16   per-feature gain (device)
+ *   eps     >= 0, finite   (else GQA_ERR_ARG; with eps = 0 an all-zero row
+ *                           gives non-finite output)
+ * and returns out = x + Δ instead of Δ. h_out, when given, is still H of the
+ * normalised input. x̂ lives in the workspace region H uses later.
+ */
+int gqa_block_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                              const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                              const gqa_bf16* w_o, const float* rope, const float* mask,
+                              int causal, int B, int T, int kv_len, float* out,
+                              gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+int gqa_chunk_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                              const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                              const gqa_bf16* w_o, const float* rope, gqa_bf16* k_cache,
+                              gqa_bf16* v_cache, int B, int T, int S_max, int start_pos,
+                              float* out, gqa_bf16* h_out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int gqa_decode_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,
+                               const gqa_bf16* w_q, const gqa_bf16* w_k, const gqa_bf16* w_v,
+                               const gqa_bf16* w_o, const float* rope, gqa_bf16* k_cache,
+                               gqa_bf16* v_cache, int B, int S_max, int start_pos, float* out,
+                               gqa_bf16* h_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * The normalisation alone (same definition as above):
+ *   x [M][4096] bf16, norm_w [4096] bf16, y [M][4096] bf16 out; 1 <= M
+ */
+int gqa_rmsnorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, gqa_bf16* y,
+                void* stream);
+
+/*
  * Stage 1 alone: Q, K, V projections with the pair rotation applied to Q and K
  * ("All 13 steps": the three projections and the rotation). Each output is
  * rounded to bf16 once, after the rotation.

@@ -53,6 +53,19 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
+def round_to_bf16(a) -> np.ndarray:
+    """Nearest bf16 value of each float64, ties to even, returned as float64.
+
+    bf16 keeps 8 significant bits (the top half of an IEEE float32): with
+    a = m·2^e, 0.5 <= |m| < 1, the result is rint(m·2^8)·2^(e-8), rint rounding
+    halves to even. Exact in fp64 (one rounding, no pass through float32);
+    values here stay far from bf16's overflow and subnormal range.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
 def _f64(a) -> np.ndarray:
     """bf16 bit patterns (uint16) or any float array -> float64."""
     a = np.asarray(a)
@@ -312,8 +325,11 @@ def block_forward_rows(x, wq, wk, wv, wo, n_heads: int, n_kv: int, rows,
 # there is RMSNorm(dim, eps=norm_eps) with norm_eps = 1e-5 (catalogue entry), but
 # no page writes its formula out. Reading taken: root-mean-square layer
 # normalisation (Zhang & Sennrich, 2019) with a learned per-feature gain and eps
-# added under the root; evaluated exactly here (the pages' own code rounds twice,
-# after the scaling and after the gain; this oracle rounds nothing).
+# added under the root, evaluated exactly.
+#
+# The attention module's input is an activation of the model's bf16 data flow
+# (as x itself is at this boundary), so by default x̂ is rounded once to bf16
+# (nearest even) before the block; input_bf16=False keeps it exact.
 
 def rms_norm(x, weight, eps: float = NORM_EPS) -> np.ndarray:
     """y[..., i] = weight[i] · x[..., i] / sqrt(mean over j of x[..., j]^2 + eps), fp64.
@@ -328,13 +344,16 @@ def rms_norm(x, weight, eps: float = NORM_EPS) -> np.ndarray:
 
 
 def prenorm_block_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, *,
-                          eps: float = NORM_EPS, **kw) -> dict:
-    """out = x + Δ_attn(rms_norm(x)): the attention half of the block with its
-    handoff (Merge and project page, handoff excerpt). Keyword arguments go to
-    block_forward (causal, mask, start_pos, caches). Returns block_forward's
-    intermediates plus x_norm and out."""
+                          eps: float = NORM_EPS, input_bf16: bool = True, **kw) -> dict:
+    """out = x + Δ_attn(x̂), x̂ = rms_norm(x) (bf16-rounded when input_bf16): the
+    attention half of the block with its handoff (Merge and project page,
+    handoff excerpt). Other keyword arguments go to block_forward (causal,
+    mask, start_pos, caches). Returns block_forward's intermediates plus
+    x_norm (x̂ as fed to the block) and out."""
     x = _f64(x)
     xn = rms_norm(x, norm_w, eps)
+    if input_bf16:
+        xn = round_to_bf16(xn)
     r = block_forward(xn, wq, wk, wv, wo, n_heads, n_kv, **kw)
     r["x_norm"] = xn
     r["out"] = x + r["delta"]
@@ -343,10 +362,13 @@ def prenorm_block_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, *,
 
 def prenorm_decode_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, k_cache,
                            v_cache, start_pos: int, eps: float = NORM_EPS,
-                           theta: float = ROPE_THETA) -> dict:
-    """decode_forward on rms_norm(x) plus the residual: out = x + Δ, x [B, d]."""
+                           theta: float = ROPE_THETA, input_bf16: bool = True) -> dict:
+    """decode_forward on x̂ = rms_norm(x) (bf16-rounded when input_bf16) plus the
+    residual: out = x + Δ, x [B, d]."""
     x = _f64(x)
     xn = rms_norm(x, norm_w, eps)
+    if input_bf16:
+        xn = round_to_bf16(xn)
     r = decode_forward(xn, wq, wk, wv, wo, n_heads, n_kv, k_cache, v_cache, start_pos, theta)
     r["x_norm"] = xn
     r["out"] = x + r["delta"]

@@ -174,3 +174,36 @@ def test_stage_entries_reject():
     assert lib.gqa_output_projection(FAKE, MIS, 3, FAKE, None) == ALIGN
     assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 2, 10, 11, FAKE, FAKE, 1 << 30, None) == SHAPE
     assert lib.gqa_decode_attention(FAKE, FAKE, FAKE, 2, 10, 10, FAKE, None, 0, None) == WORKSPACE
+
+
+def test_prenorm_entries_reject():
+    lib = gqa.lib()
+    # the stage: rows, pointers, eps and alignment
+    assert lib.gqa_rmsnorm(FAKE, FAKE, 1e-5, 0, FAKE, None) == SHAPE
+    assert lib.gqa_rmsnorm(None, FAKE, 1e-5, 4, FAKE, None) == NULL
+    assert lib.gqa_rmsnorm(FAKE, None, 1e-5, 4, FAKE, None) == NULL
+    assert lib.gqa_rmsnorm(FAKE, FAKE, -1e-5, 4, FAKE, None) == ARG
+    assert lib.gqa_rmsnorm(FAKE, FAKE, float("nan"), 4, FAKE, None) == ARG
+    assert lib.gqa_rmsnorm(FAKE, FAKE, float("inf"), 4, FAKE, None) == ARG
+    assert lib.gqa_rmsnorm(FAKE, MIS, 1e-5, 4, FAKE, None) == ALIGN
+    assert lib.gqa_rmsnorm(FAKE, FAKE, 1e-5, 4, MIS, None) == ALIGN
+    # the half-block forms: the gain checks come on top of the plain entry's
+    blk = lambda g, eps, **kw: lib.gqa_block_forward_prenorm(
+        kw.get("x", FAKE), g, eps, FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, kw.get("T", 128),
+        kw.get("T", 128), FAKE, None, kw.get("ws", FAKE), 1 << 40, None)
+    assert blk(None, 1e-5) == NULL
+    assert blk(FAKE, -1.0) == ARG
+    assert blk(MIS, 1e-5) == ALIGN
+    assert blk(FAKE, 1e-5, x=None) == NULL
+    assert blk(FAKE, 1e-5, T=0) == SHAPE
+    assert blk(FAKE, 1e-5, ws=None) == WORKSPACE
+    dec = lambda g, eps, sp=10: lib.gqa_decode_forward_prenorm(
+        FAKE, g, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 16, sp, FAKE, None, FAKE,
+        1 << 40, None)
+    assert dec(None, 1e-5) == NULL and dec(FAKE, float("nan")) == ARG
+    assert dec(FAKE, 1e-5, sp=16) == SHAPE
+    chk = lambda g, eps, sp=8: lib.gqa_chunk_forward_prenorm(
+        FAKE, g, eps, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 16, sp, FAKE, None, FAKE,
+        1 << 40, None)
+    assert chk(None, 1e-5) == NULL and chk(FAKE, -2.0) == ARG
+    assert chk(FAKE, 1e-5, sp=9) == SHAPE

@@ -351,10 +351,16 @@ def test_prenorm_residual_adds_x_to_the_normalised_block():
     # leaves that part unchanged (eps = 0), so out(αx) − αx = out(x) − x.
     x, wq, wk, wv, wo, kc, vc = _tiny(22, B=1, T=6)
     g = 1.0 + np.random.default_rng(5).standard_normal(16) * 0.3
-    r1 = O.prenorm_block_forward(x, g, wq, wk, wv, wo, 4, 2, eps=0.0)
-    r2 = O.prenorm_block_forward(3.5 * x, g, wq, wk, wv, wo, 4, 2, eps=0.0)
+    r1 = O.prenorm_block_forward(x, g, wq, wk, wv, wo, 4, 2, eps=0.0, input_bf16=False)
+    r2 = O.prenorm_block_forward(3.5 * x, g, wq, wk, wv, wo, 4, 2, eps=0.0, input_bf16=False)
     assert np.allclose(r2["out"] - 3.5 * x, r1["out"] - x, rtol=1e-10, atol=1e-12)
     assert not np.allclose(r1["out"] - x, O.block_forward(x, wq, wk, wv, wo, 4, 2)["delta"])
+    # with the bf16 input reading, the block sees the rounded x̂
+    r3 = O.prenorm_block_forward(x, g, wq, wk, wv, wo, 4, 2, eps=0.0)
+    xr = O.round_to_bf16(O.rms_norm(x, g, eps=0.0))
+    assert np.array_equal(r3["x_norm"], xr)
+    assert np.allclose(r3["out"] - x, O.block_forward(xr, wq, wk, wv, wo, 4, 2)["delta"],
+                       rtol=1e-12, atol=1e-14)
     # decode form: same block at one position over the cache
     x, wq, wk, wv, wo, kc, vc = _tiny(23, B=2, T=1, cache=4)
     d = O.prenorm_decode_forward(x[:, 0], g, wq, wk, wv, wo, 4, 2, kc, vc, 3)
@@ -369,3 +375,23 @@ def test_norm_gain_generator_is_seeded_and_centred():
     v = O.bf16_to_f64(g1)
     assert abs(v.mean() - 1.0) < 0.02 and 0.17 < v.std() < 0.23
     assert not np.array_equal(g1, gi.make_norm_weight(4))
+
+
+def test_round_to_bf16_known_values_and_ties_to_even():
+    # bf16 spacing is 2^-7 in [1, 2): 1 + 2^-8 is a tie and goes to the even
+    # neighbour 1; 1 + 3·2^-8 is a tie between 1 + 2^-7 (odd) and 1 + 2^-6 (even)
+    cases = {1.0: 1.0, 1.0 + 2 ** -8: 1.0, 1.0 + 3 * 2 ** -8: 1.0 + 2 ** -6,
+             1.0 + 2 ** -8 + 2 ** -30: 1.0 + 2 ** -7, -(1.0 + 2 ** -8 + 2 ** -30): -(1.0 + 2 ** -7),
+             0.0: 0.0, 3.0: 3.0, 255.5: 256.0, 2.0 ** -130: 2.0 ** -130, 1e-3: 0.00099945068359375}
+    for a, want in cases.items():
+        assert O.round_to_bf16(np.array([a]))[0] == want, a
+    # agrees with the generator's float32 -> bf16 rounding wherever float32 is exact
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal(20000) * np.exp(rng.uniform(-20, 20, 20000))).astype(np.float32)
+    assert np.array_equal(O.round_to_bf16(v.astype(np.float64)),
+                          O.bf16_to_f64(gi.f32_to_bf16_bits(v)))
+    # and lands within half a bf16 ulp of fp64 inputs that float32 cannot hold
+    w = rng.standard_normal(20000) * 10.0
+    r = O.round_to_bf16(w)
+    _, e = np.frexp(w)
+    assert np.all(np.abs(r - w) <= np.ldexp(0.5, e - 8))
