@@ -52,6 +52,7 @@ def _load():
         "gqa_status_string": (ctypes.c_char_p, [I]),
         "gqa_dims": (None, [P, P, P, P]),
         "gqa_rope_table": (I, [P, I, D, P]),
+        "gqa_rope_table_freqs": (I, [P, I, P, P]),
         "gqa_prefill_workspace_bytes": (Z, [I, I]),
         "gqa_decode_workspace_bytes": (Z, [I, I]),
         "gqa_attention_workspace_bytes": (Z, [I, I, I, I]),
@@ -85,7 +86,8 @@ def lib():
 
 
 def exported_symbols():
-    return ["gqa_status_string", "gqa_dims", "gqa_rope_table", "gqa_prefill_workspace_bytes",
+    return ["gqa_status_string", "gqa_dims", "gqa_rope_table", "gqa_rope_table_freqs",
+            "gqa_prefill_workspace_bytes",
             "gqa_decode_workspace_bytes", "gqa_attention_workspace_bytes",
             "gqa_chunk_workspace_bytes", "gqa_block_forward", "gqa_chunk_forward",
             "gqa_decode_forward",
@@ -135,13 +137,23 @@ def dims():
     return a.value, b.value, c.value, d.value
 
 
-def rope_table(positions, theta: float = ROPE_THETA) -> np.ndarray:
-    """(cos, sin) table [n, 64, 2] float32 for the given positions (host computation)."""
+def rope_table(positions, theta: float = ROPE_THETA, omega=None) -> np.ndarray:
+    """(cos, sin) table [n, 64, 2] float32 for the given positions (host computation).
+
+    omega: optional 64 explicit per-pair frequencies in place of theta^(-2j/128).
+    """
     pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
     out = np.empty((pos.size, N_PAIRS, 2), dtype=np.float32)
-    _check("gqa_rope_table", _load().gqa_rope_table(
-        pos.ctypes.data if pos.size else None, int(pos.size), float(theta),
-        out.ctypes.data if pos.size else None))
+    pp = pos.ctypes.data if pos.size else None
+    po = out.ctypes.data if pos.size else None
+    if omega is None:
+        _check("gqa_rope_table", _load().gqa_rope_table(pp, int(pos.size), float(theta), po))
+    else:
+        w = np.ascontiguousarray(np.asarray(omega, dtype=np.float64))
+        if w.shape != (N_PAIRS,):
+            raise ValueError(f"omega: expected {N_PAIRS} frequencies, got shape {w.shape}")
+        _check("gqa_rope_table_freqs",
+               _load().gqa_rope_table_freqs(pp, int(pos.size), w.ctypes.data, po))
     return out
 
 

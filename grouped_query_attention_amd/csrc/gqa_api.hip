@@ -270,6 +270,16 @@ int gqa_rope_table(const int32_t* positions, int n, double theta, float* table) 
   double omega[GQA_N_PAIRS];
   for (int j = 0; j < GQA_N_PAIRS; ++j)
     omega[j] = std::exp(-(2.0 * j / (double)GQA_D_HEAD) * std::log(theta));
+  return gqa_rope_table_freqs(positions, n, omega, table);
+}
+
+int gqa_rope_table_freqs(const int32_t* positions, int n, const double* omega, float* table) {
+  if (n < 0) return GQA_ERR_SHAPE;
+  if (!omega) return GQA_ERR_NULL;
+  for (int j = 0; j < GQA_N_PAIRS; ++j)
+    if (!std::isfinite(omega[j])) return GQA_ERR_ARG;
+  if (n == 0) return GQA_OK;
+  if (!positions || !table) return GQA_ERR_NULL;
   for (int i = 0; i < n; ++i) {
     const double t = (double)positions[i];
     for (int j = 0; j < GQA_N_PAIRS; ++j) {

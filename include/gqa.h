@@ -77,6 +77,22 @@ void gqa_dims(int* d_model, int* n_heads, int* n_kv_heads, int* d_head);
  */
 int gqa_rope_table(const int32_t* positions, int n, double theta, float* table);
 
+/*
+ * Rotation table R from explicit per-pair frequencies (host-side helper, no
+ * GPU call). The block takes R as an input (Grouped-query attention page,
+ * in/out header) and the rotation in "All 13 steps" uses frequencies ω'_j:
+ * callers whose frequencies are not theta^(-2j/128) (rescaled ones for long
+ * contexts, as the 3.1 catalogue entry's use_scaled_rope flag asks for; the
+ * rescaling rule itself is not on the pages) build their table here. The
+ * kernels apply whatever table they are given.
+ *   positions (host) [n], omega (host) [64] finite frequencies (rad/position)
+ *   table     (host) [n][64][2]  out: (cos(t·omega_j), sin(t·omega_j)),
+ *                                double precision, stored as float
+ * Returns GQA_ERR_NULL / GQA_ERR_SHAPE (n < 0) / GQA_ERR_ARG (a non-finite
+ * omega) or GQA_OK.
+ */
+int gqa_rope_table_freqs(const int32_t* positions, int n, const double* omega, float* table);
+
 /* Workspace bytes gqa_block_forward needs for B sequences of T positions. */
 size_t gqa_prefill_workspace_bytes(int B, int T);
 

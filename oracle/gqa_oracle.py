@@ -100,10 +100,17 @@ def rope_frequencies(d_head: int, theta: float = ROPE_THETA) -> np.ndarray:
     return np.exp(-(2.0 * j / d_head) * math.log(theta))
 
 
-def rope_cos_sin(positions, d_head: int, theta: float = ROPE_THETA):
-    """cos(t·ω_j), sin(t·ω_j) in fp64, shape [len(positions), d_head/2]."""
+def rope_cos_sin(positions, d_head: int, theta: float = ROPE_THETA, omega=None):
+    """cos(t·ω_j), sin(t·ω_j) in fp64, shape [len(positions), d_head/2].
+
+    `omega` (d_head/2 frequencies) replaces θ^(-2j/d_head) when given: the
+    block takes the table R as an input (Grouped-query attention page, in/out
+    header), and the prime on ω in "All 13 steps" allows frequencies other
+    than the plain ones (the 3.1 catalogue entry sets use_scaled_rope).
+    """
     t = np.asarray(positions, dtype=np.float64)
-    ang = np.outer(t, rope_frequencies(d_head, theta))
+    w = rope_frequencies(d_head, theta) if omega is None else np.asarray(omega, np.float64)
+    ang = np.outer(t, w)
     return np.cos(ang), np.sin(ang)
 
 
@@ -204,7 +211,7 @@ def merge_heads(h: np.ndarray) -> np.ndarray:
 def block_forward(x, wq, wk, wv, wo, n_heads: int, n_kv: int, *, causal: bool = True,
                   mask: Optional[np.ndarray] = None, start_pos: int = 0,
                   k_cache=None, v_cache=None, theta: float = ROPE_THETA,
-                  return_probs: bool = False) -> dict:
+                  return_probs: bool = False, omega=None) -> dict:
     """Δ_attn for x [B, T, d] (bf16 bits or float arrays), all in fp64.
 
     causal=True builds the mask of the model.py excerpt for this T and
@@ -223,7 +230,7 @@ def block_forward(x, wq, wk, wv, wo, n_heads: int, n_kv: int, *, causal: bool = 
     k = split_heads(project(x, wk), n_kv)
     v = split_heads(project(x, wv), n_kv)
     dh = q.shape[-1]
-    cos, sin = rope_cos_sin(np.arange(start_pos, start_pos + T), dh, theta)
+    cos, sin = rope_cos_sin(np.arange(start_pos, start_pos + T), dh, theta, omega)
     q_r = rope_rotate(q, cos, sin)
     k_r = rope_rotate(k, cos, sin)
     if start_pos > 0:

@@ -62,6 +62,21 @@ def test_rope_table_matches_oracle_trig():
     assert lib.gqa_rope_table(None, 0, 500000.0, None) == OK
 
 
+def test_rope_table_from_frequencies():
+    pos = np.array([0, 3, 8191, 100000], dtype=np.int32)
+    w = O.rope_frequencies(128) / np.linspace(1.0, 8.0, 64)
+    tab = gqa.rope_table(pos, omega=w)
+    c, s = O.rope_cos_sin(pos, 128, omega=w)
+    assert np.max(np.abs(tab[..., 0] - c)) < 1e-7 and np.max(np.abs(tab[..., 1] - s)) < 1e-7
+    # the plain frequencies give the theta table
+    assert np.array_equal(gqa.rope_table(pos, omega=O.rope_frequencies(128)), gqa.rope_table(pos))
+    lib = gqa.lib()
+    bad = np.full(64, np.nan)
+    assert lib.gqa_rope_table_freqs(pos.ctypes.data, 4, bad.ctypes.data, tab.ctypes.data) == ARG
+    assert lib.gqa_rope_table_freqs(pos.ctypes.data, 4, None, tab.ctypes.data) == NULL
+    assert lib.gqa_rope_table_freqs(pos.ctypes.data, -1, w.ctypes.data, tab.ctypes.data) == SHAPE
+
+
 def test_workspace_sizes():
     M = 8 * 4096   # enough query tiles: no balanced-attention partials, no split reduction
     want = sum(((M * f * 2 + 255) // 256) * 256 for f in (4096, 1024, 1024, 4096))

@@ -331,3 +331,44 @@ def test_decode_matches_prefill_row():
     ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)["delta"][:, p]
     assert_close(f32_to_np_f64(out), ref, what="decode row p")
     assert_close(f32_to_np_f64(out), f32_to_np_f64(full[:, p]), what="decode vs prefill")
+
+
+# --- rotation tables from explicit frequencies -------------------------------------------
+
+def _rescaled_omega():
+    # a long-context style table: low-frequency pairs divided by up to 8 (a
+    # synthetic ramp; the kernels apply whatever table they are given)
+    return O.rope_frequencies(128) / np.linspace(1.0, 8.0, 64)
+
+
+def test_block_forward_rescaled_table():
+    print("[case] block_forward B=2 T=300 rescaled frequencies", flush=True)
+    B, T = 2, 300
+    w = _rescaled_omega()
+    inp = gi.make_block_inputs(41, B, T)
+    wq, wk, wv, wo = _weights(inp)
+    rope = to_dev_f32(gqa.rope_table(np.arange(T), omega=w))
+    out = gqa.block_forward(to_dev_bf16(inp.x), wq, wk, wv, wo, rope)
+    torch.cuda.synchronize()
+    ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8, omega=w)
+    assert_close(f32_to_np_f64(out), ref["delta"], what="Δ rescaled table")
+    plain = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)["delta"]
+    assert np.linalg.norm(plain - ref["delta"]) > 0.05 * np.linalg.norm(plain)
+
+
+def test_chunk_forward_rescaled_table_far_positions():
+    # positions 20000 .. 20063 over 20000 cached ones, past the 8192 positions of
+    # the unscaled catalogue entry's context
+    print("[case] chunk B=1 T=64 start_pos=20000 rescaled frequencies", flush=True)
+    B, T, sp = 1, 64, 20000
+    w = _rescaled_omega()
+    inp = gi.make_block_inputs(42, B, T, cache_len=sp + T)
+    wq, wk, wv, wo = _weights(inp)
+    kc, vc = to_dev_bf16(inp.k_cache), to_dev_bf16(inp.v_cache)
+    rope = to_dev_f32(gqa.rope_table(np.arange(sp, sp + T), omega=w))
+    out = gqa.chunk_forward(to_dev_bf16(inp.x), wq, wk, wv, wo, rope, kc, vc, sp)
+    torch.cuda.synchronize()
+    ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8, start_pos=sp,
+                          k_cache=inp.k_cache, v_cache=inp.v_cache, omega=w)
+    assert_close(f32_to_np_f64(out), ref["delta"], what="Δ chunk rescaled")
+    assert_close(bf16_to_np_f64(kc)[:, sp:], ref["k_r"], rel=STAGE_REL, what="cache K rescaled")

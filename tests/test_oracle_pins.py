@@ -395,3 +395,20 @@ def test_round_to_bf16_known_values_and_ties_to_even():
     r = O.round_to_bf16(w)
     _, e = np.frexp(w)
     assert np.all(np.abs(r - w) <= np.ldexp(0.5, e - 8))
+
+
+def test_rope_explicit_frequencies():
+    # the table is an input of the block: explicit frequencies replace θ^(-2j/d)
+    x, wq, wk, wv, wo, _, _ = _tiny(31, B=1, T=5)
+    base = O.block_forward(x, wq, wk, wv, wo, 4, 2)
+    same = O.block_forward(x, wq, wk, wv, wo, 4, 2, omega=O.rope_frequencies(4))
+    assert np.array_equal(base["delta"], same["delta"])
+    # zero frequencies: no rotation at any position
+    flat = O.block_forward(x, wq, wk, wv, wo, 4, 2, omega=np.zeros(2))
+    assert np.array_equal(flat["q_r"], flat["q"]) and np.array_equal(flat["k_r"], flat["k"])
+    # dividing every frequency by 8 (exact in binary) turns position 8t into t
+    w = O.rope_frequencies(128)
+    t = np.array([0, 1, 5, 1000, 8191])
+    c1, s1 = O.rope_cos_sin(8 * t, 128, omega=w / 8)
+    c2, s2 = O.rope_cos_sin(t, 128)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
