@@ -12,7 +12,10 @@ attention" page, parameter table and in/out header):
   * block input x [B, T, 4096] ~ N(0, 1);
   * decode K/V cache [B, S_max, 8, 128] ~ N(0, 1);
   * gain of the pre-attention RMS normalisation [4096] ~ 1 + N(0, 0.2^2), from
-    a stream of its own (make_norm_weight).
+    a stream of its own (make_norm_weight);
+  * SwiGLU MLP ("Llama 3" page): w1, w3 [14336, 4096], w2 [4096, 14336] ~
+    N(0, 0.02^2), input [M, 4096] ~ N(0, 1), from a stream of their own
+    (make_mlp_inputs).
 Each value is drawn as a float32 standard normal from numpy's PCG64 generator,
 scaled by the standard deviation in float32 and rounded to bf16 with
 round-to-nearest-even. Generation order: W_Q, W_K, W_V, W_O, x, cache K,
@@ -30,6 +33,7 @@ D_MODEL = 4096
 N_HEADS = 32
 N_KV_HEADS = 8
 D_HEAD = 128
+D_FF = 14336
 
 _CHUNK = 1 << 24  # values drawn per step, bounds the float32 temporaries
 
@@ -91,6 +95,28 @@ def make_block_inputs(seed: int, B: int, T: int, *, d: int = D_MODEL,
         kc = normal_bf16(rng, (B, cache_len, n_kv, d_head), cache_std)
         vc = normal_bf16(rng, (B, cache_len, n_kv, d_head), cache_std)
     return BlockInputs(x=x, wq=wq, wk=wk, wv=wv, wo=wo, k_cache=kc, v_cache=vc)
+
+
+@dataclass
+class MlpInputs:
+    """bf16 bit patterns (uint16) of the SwiGLU MLP's weights and input."""
+
+    x: np.ndarray            # [M, d]
+    w1: np.ndarray           # [d_ff, d]  gate
+    w3: np.ndarray           # [d_ff, d]  up
+    w2: np.ndarray           # [d, d_ff]  down
+
+
+def make_mlp_inputs(seed: int, M: int, *, d: int = D_MODEL, d_ff: int = D_FF,
+                    w_std: float = 0.02, x_std: float = 1.0) -> MlpInputs:
+    """Seeded MLP weights N(0, w_std^2) and input N(0, x_std^2), bf16 (nearest
+    even). Generation order: w1, w3, w2, x."""
+    rng = np.random.Generator(np.random.PCG64(seed + 15485863))
+    w1 = normal_bf16(rng, (d_ff, d), w_std)
+    w3 = normal_bf16(rng, (d_ff, d), w_std)
+    w2 = normal_bf16(rng, (d, d_ff), w_std)
+    x = normal_bf16(rng, (M, d), x_std)
+    return MlpInputs(x=x, w1=w1, w3=w3, w2=w2)
 
 
 def make_norm_weight(seed: int, d: int = D_MODEL, std: float = 0.2) -> np.ndarray:

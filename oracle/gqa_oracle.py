@@ -382,6 +382,50 @@ def prenorm_decode_forward(x, norm_w, wq, wk, wv, wo, n_heads: int, n_kv: int, k
     return r
 
 
+# --- the other half of the block: SwiGLU MLP ---------------------------------------------
+#
+# "Llama 3" page, section "SwiGLU MLP": three bias-free projections w1, w3
+# (d -> d_ff) and w2 (d_ff -> d), stored [out, in] like the attention weights;
+# output w2(silu(w1 x) * w3 x), silu(g) = g·σ(g), σ(z) = 1/(1 + e^-z); d_ff =
+# 14336 (the SiLU panel's shapes). The block feeds it ffn_norm(h) and adds its
+# update to h (Merge and project page, handoff excerpt): the same RMS
+# normalisation and residual as the attention half.
+
+D_FF = 14336
+
+
+def silu(g) -> np.ndarray:
+    """silu(g) = g / (1 + e^-g) in fp64 ("Llama 3" page, SiLU explanation).
+    For g below about -709, e^-g overflows to inf and the value is -0, the limit."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def mlp_forward(x, w1, w2, w3) -> dict:
+    """out = w2(silu(w1 x) · w3 x) for x [..., d], all in fp64.
+    Returns the gate g = x·w1ᵀ, up u = x·w3ᵀ, a = silu(g)·u and delta = a·w2ᵀ."""
+    x, w1, w2, w3 = (_f64(t) for t in (x, w1, w2, w3))
+    g = project(x, w1)
+    u = project(x, w3)
+    a = silu(g) * u
+    return dict(g=g, u=u, a=a, delta=project(a, w2))
+
+
+def prenorm_mlp_forward(h, norm_w, w1, w2, w3, eps: float = NORM_EPS,
+                        input_bf16: bool = True) -> dict:
+    """out = h + mlp(ĥ), ĥ = rms_norm(h) (bf16-rounded when input_bf16, the MLP's
+    input being a bf16 activation), h [..., d]."""
+    h = _f64(h)
+    hn = rms_norm(h, norm_w, eps)
+    if input_bf16:
+        hn = round_to_bf16(hn)
+    r = mlp_forward(hn, w1, w2, w3)
+    r["x_norm"] = hn
+    r["out"] = h + r["delta"]
+    return r
+
+
 def param_counts(d: int, n_heads: int, n_kv: int) -> dict:
     """Weight-element counts of one block for the given dims (head width d/n_heads)."""
     dh = d // n_heads

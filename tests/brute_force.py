@@ -71,3 +71,16 @@ def brute_block(x, wq, wk, wv, wo, n_heads, n_kv, start_pos=0, cache_k=None,
             rows.append(_linear(merged, wo))
         out.append(rows)
     return out
+
+
+def brute_mlp(x, w1, w2, w3):
+    """x: [T][d] lists; w1, w3: [f][d]; w2: [d][f]. Written from the "Llama 3"
+    page's SwiGLU MLP (w2(silu(w1 x) * w3 x), silu(g) = g * sigma(g),
+    sigma(z) = 1/(1 + e^-z)) with loops. Returns [T][d]."""
+    out = []
+    for row in x:
+        gate = _linear(row, w1)
+        up = _linear(row, w3)
+        a = [gi * (1.0 / (1.0 + math.exp(-gi))) * ui for gi, ui in zip(gate, up)]
+        out.append(_linear(a, w2))
+    return out

@@ -412,3 +412,68 @@ def test_rope_explicit_frequencies():
     c1, s1 = O.rope_cos_sin(8 * t, 128, omega=w / 8)
     c2, s2 = O.rope_cos_sin(t, 128)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+
+
+# --- SwiGLU MLP -------------------------------------------------------------------------
+
+def test_silu_minimum_matches_page():
+    # the page prints that SiLU dips to about -0.28 near g = -1.28
+    from scipy.optimize import minimize_scalar
+    gold = _golden("llama3_swiglu_page.json")
+    r = minimize_scalar(lambda g: float(O.silu(g)), bounds=(-5, 5), method="bounded",
+                        options={"xatol": 1e-10})
+    nd = gold["printed_decimals"]
+    assert round(r.x, nd) == gold["silu_min_at_about"]
+    assert round(r.fun, nd) == gold["silu_min_value_about"]
+    assert O.D_FF == gold["d_ff"]
+
+
+def test_silu_identities():
+    g = np.linspace(-30, 30, 601)
+    # sigma(g) + sigma(-g) = 1  =>  silu(g) - silu(-g) = g
+    assert np.allclose(O.silu(g) - O.silu(-g), g, rtol=1e-13, atol=1e-13)
+    assert O.silu(0.0) == 0.0
+    assert O.silu(50.0) == 50.0                       # sigma(50) rounds to 1
+    assert O.silu(-800.0) == 0.0                      # the limit, no overflow error
+    # slope 1/2 at 0 (sigma(0) = 1/2)
+    e = 1e-6
+    assert abs((O.silu(e) - O.silu(-e)) / (2 * e) - 0.5) < 1e-9
+    assert abs(O.silu(1.0) - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+
+
+def test_mlp_brute_force_tiny():
+    from tests.brute_force import brute_mlp
+    rng = np.random.default_rng(17)
+    T, d, f = 3, 5, 7     # non-square: a transposed weight cannot pass
+    x = rng.standard_normal((T, d))
+    w1, w3 = rng.standard_normal((f, d)), rng.standard_normal((f, d))
+    w2 = rng.standard_normal((d, f))
+    want = np.array(brute_mlp(x.tolist(), w1.tolist(), w2.tolist(), w3.tolist()))
+    got = O.mlp_forward(x, w1, w2, w3)["delta"]
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12)
+    # gate and up are not interchangeable (silu is not symmetric)
+    assert not np.allclose(O.mlp_forward(x, w3, w2, w1)["delta"], want)
+
+
+def test_mlp_structure():
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal((4, 6))
+    w1, w3, w2 = rng.standard_normal((9, 6)), rng.standard_normal((9, 6)), rng.standard_normal((6, 9))
+    r = O.mlp_forward(x, w1, w2, w3)
+    # linear in w2 and in w3; zero up projection gives zero output
+    assert np.allclose(O.mlp_forward(x, w1, 2.5 * w2, w3)["delta"], 2.5 * r["delta"], rtol=1e-13)
+    assert np.allclose(O.mlp_forward(x, w1, w2, -3 * w3)["delta"], -3 * r["delta"], rtol=1e-13)
+    assert np.array_equal(O.mlp_forward(x, w1, w2, 0 * w3)["delta"], np.zeros((4, 6)))
+    # rows are independent: one row alone gives the same row
+    assert np.allclose(O.mlp_forward(x[2:3], w1, w2, w3)["delta"], r["delta"][2:3], rtol=1e-13)
+    # pre-norm form: zero gain leaves h unchanged (silu(0)·0 = 0)
+    p = O.prenorm_mlp_forward(x, np.zeros(6), w1, w2, w3)
+    assert np.array_equal(p["out"], x)
+
+
+def test_mlp_generator_shapes():
+    m = gi.make_mlp_inputs(1, 3)
+    assert m.w1.shape == (14336, 4096) and m.w3.shape == (14336, 4096)
+    assert m.w2.shape == (4096, 14336) and m.x.shape == (3, 4096)
+    small = gi.make_mlp_inputs(1, 3, d=32, d_ff=64)
+    assert np.array_equal(small.x, gi.make_mlp_inputs(1, 3, d=32, d_ff=64).x)
