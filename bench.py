@@ -7,8 +7,8 @@ TFLOP/s of algorithmic work (only unmasked query/key pairs count). Also
 measured in the same run: decode (B=64, one token at position 8191 over a
 bf16 KV cache of 8192 rows) in HBM GB/s, chunked prefill (B=1, 2048 new
 positions after 2048 cached ones), the pre-norm + residual forms of the
-headline prefill and of decode, and prefill at B=8, T=4096 and at B=1,
-T=131072.
+headline prefill and of decode, the pre-norm SwiGLU MLP at 2048 and 64
+tokens, and prefill at B=8, T=4096 and at B=1, T=131072.
 
 Prints one JSON line. Inputs are seeded synthetic bf16 values resident in HBM
 before the timed region. `roofline` describes the kernel that takes the most
@@ -17,7 +17,7 @@ time in the headline step, timed with HIP events on the stream it runs on;
 workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
-       python bench.py --only decode|chunk|prenorm|prefill_B8_T4096|prefill_B1_T131072
+       python bench.py --only decode|chunk|prenorm|mlp|prefill_B8_T4096|prefill_B1_T131072
 """
 
 import argparse
@@ -334,6 +334,39 @@ class Bench:
         del kc, vc, dws
         torch.cuda.empty_cache()
 
+    # ---------------- SwiGLU MLP (the block's other half) ----------------
+    def mlp(self, extra):
+        """Pre-norm SwiGLU MLP with its residual: M = 2048 tokens (the headline's
+        tokens) in TFLOP/s, and M = 64 (one decode step of 64 sequences) in HBM GB/s
+        of weights."""
+        torch, gqa, args = self.torch, self.gqa, self.args
+        self.log("[bench] SwiGLU MLP: generating weights")
+        m = self.gi.make_mlp_inputs(8, 2048)
+        w1, w2, w3 = (self.up(a) for a in (m.w1, m.w2, m.w3))
+        x = self.up(m.x)
+        g = self.up(self.gi.make_norm_weight(8))
+        del m
+        for M in (2048, 64):
+            xm = x[:M].contiguous()
+            out = torch.empty((M, 4096), dtype=torch.float32, device=self.dev)
+            ws = torch.empty(gqa.mlp_workspace_bytes(M), dtype=torch.uint8, device=self.dev)
+            step = lambda: gqa.mlp_forward(xm, w1, w2, w3, norm_w=g, out=out, workspace=ws)
+            ms, _ = self.time_steps(step, args.steps, args.warmup)
+            F = 3 * 2 * M * 4096 * 14336
+            wbytes = 3 * 4096 * 14336 * 2
+            rec = {"ms": round(ms, 5), "TFLOP/s": round(F / (ms * 1e-3) / 1e12, 1),
+                   "frac_of_bf16_peak": round(F / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "flops_per_step": F}
+            if M <= 64:
+                nb = wbytes + M * 4096 * (2 + 4)
+                rec.update({"GB/s": round(nb / (ms * 1e-3) / 1e9, 1),
+                            "frac_of_hbm": round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                            "bytes_per_step": nb})
+            extra[f"mlp_prenorm_M{M}"] = rec
+            self.log(f"[bench] MLP M={M}: {ms:.4f} ms, {rec['TFLOP/s']} TFLOP/s")
+        del w1, w2, w3, x
+        torch.cuda.empty_cache()
+
     def prefill_b8(self, extra):
         self.prefill(extra, 8, 4096, 3, max(3, self.args.steps // 4))
 
@@ -382,7 +415,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--only", choices=["decode", "chunk", "prenorm", "prefill_B8_T4096",
+    ap.add_argument("--only", choices=["decode", "chunk", "prenorm", "mlp", "prefill_B8_T4096",
                                        "prefill_B1_T131072"],
                     help="run just this one workload and print its figures (for profiling)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -398,7 +431,7 @@ def main():
     if args.calibrate_copy:
         b.calibrate_copy(args.calibrate_copy)
         return
-    others = {"decode": b.decode, "chunk": b.chunk, "prenorm": b.prenorm,
+    others = {"decode": b.decode, "chunk": b.chunk, "prenorm": b.prenorm, "mlp": b.mlp,
               "prefill_B8_T4096": b.prefill_b8,
               "prefill_B1_T131072": b.prefill_long}
     if args.only:

@@ -23,6 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgqa.so")
 
 D_MODEL, N_HEADS, N_KV_HEADS, D_HEAD, N_PAIRS = 4096, 32, 8, 128, 64
+D_FF = 14336
 ROPE_THETA = 500000.0
 NORM_EPS = 1e-5
 
@@ -71,6 +72,9 @@ def _load():
         "gqa_decode_forward_prenorm": (I, [P, P, F, P, P, P, P, P, P, P, I, I, I, P, P, P, Z,
                                            P]),
         "gqa_rmsnorm": (I, [P, P, F, I, P, P]),
+        "gqa_mlp_workspace_bytes": (Z, [I]),
+        "gqa_mlp_forward": (I, [P, P, P, P, I, P, P, P, Z, P]),
+        "gqa_mlp_forward_prenorm": (I, [P, P, F, P, P, P, I, P, P, P, Z, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -93,7 +97,8 @@ def exported_symbols():
             "gqa_decode_forward",
             "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention",
             "gqa_block_forward_prenorm", "gqa_chunk_forward_prenorm",
-            "gqa_decode_forward_prenorm", "gqa_rmsnorm"]
+            "gqa_decode_forward_prenorm", "gqa_rmsnorm", "gqa_mlp_workspace_bytes",
+            "gqa_mlp_forward", "gqa_mlp_forward_prenorm"]
 
 
 # --- helpers -------------------------------------------------------------------------
@@ -287,6 +292,44 @@ def rmsnorm(x, norm_w, eps: float = NORM_EPS, *, y=None, stream=None):
     _check("gqa_rmsnorm", _load().gqa_rmsnorm(_ptr(x), _ptr(norm_w), float(eps), M, _ptr(y),
                                               _stream(stream)))
     return y
+
+
+def mlp_workspace_bytes(M: int) -> int:
+    return int(_load().gqa_mlp_workspace_bytes(M))
+
+
+def mlp_forward(x, w1, w2, w3, *, norm_w=None, eps: float = NORM_EPS, out=None, a_out=None,
+                workspace=None, stream=None):
+    """SwiGLU MLP: out = w2(silu(x·w1ᵀ)·(x·w3ᵀ)) for x [..., 4096] bf16; fp32 out of
+    the same leading shape. With norm_w the MLP reads RMSNorm(x) and out = x + MLP."""
+    import torch
+    _req(x, torch.bfloat16, None, "x")
+    if x.shape[-1] != D_MODEL:
+        raise ValueError(f"x: last dimension must be {D_MODEL}")
+    M = x.numel() // D_MODEL
+    _req(w1, torch.bfloat16, (D_FF, D_MODEL), "w1")
+    _req(w3, torch.bfloat16, (D_FF, D_MODEL), "w3")
+    _req(w2, torch.bfloat16, (D_MODEL, D_FF), "w2")
+    if out is None:
+        out = torch.empty(tuple(x.shape), dtype=torch.float32, device=x.device)
+    _req(out, torch.float32, tuple(x.shape), "out")
+    if a_out is not None:
+        _req(a_out, torch.bfloat16, None, "a_out")
+        if a_out.numel() != M * D_FF:
+            raise ValueError(f"a_out: expected {M * D_FF} elements")
+    if workspace is None:
+        workspace = torch.empty(mlp_workspace_bytes(M), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    if norm_w is None:
+        _check("gqa_mlp_forward", _load().gqa_mlp_forward(
+            _ptr(x), _ptr(w1), _ptr(w2), _ptr(w3), M, _ptr(out), _ptr(a_out), _ptr(workspace),
+            wsb, _stream(stream)))
+    else:
+        _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
+        _check("gqa_mlp_forward_prenorm", _load().gqa_mlp_forward_prenorm(
+            _ptr(x), _ptr(norm_w), float(eps), _ptr(w1), _ptr(w2), _ptr(w3), M, _ptr(out),
+            _ptr(a_out), _ptr(workspace), wsb, _stream(stream)))
+    return out
 
 
 def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None):

@@ -38,15 +38,16 @@ namespace gqa {
 
 constexpr int BK = 64;  // K step
 
-enum Epilogue { EPI_QKV_ROPE = 0, EPI_OUT_F32 = 1, EPI_PARTIAL_F32 = 2 };
+enum Epilogue { EPI_QKV_ROPE = 0, EPI_OUT_F32 = 1, EPI_PARTIAL_F32 = 2, EPI_SWIGLU = 3 };
 
 struct GemmArgs {
-  const uint16_t* act;   // [M][4096] bf16 activations
-  const uint16_t* w0;    // weight rows (W_Q, or W_O)
-  const uint16_t* w1;    // fused QKV: W_K rows
+  const uint16_t* act;   // [M][K] bf16 activations
+  const uint16_t* w0;    // weight rows [.][K] (W_Q, W_O, the MLP's gate w1 or down w2)
+  const uint16_t* w1;    // fused QKV: W_K rows; gate/up product: up (w3) rows
   const uint16_t* w2;    // fused QKV: W_V rows
   int M;                 // tokens
-  int N;                 // output features (6144 or 4096)
+  int N;                 // output features (6144, 4096, or 2 x 14336 gate/up)
+  int K;                 // reduction length (4096, or 14336 for the MLP's down product)
   // rotation epilogue
   const float* rope;     // [T][64][2]
   int T;                 // tokens per sequence (rope row = token % T)
@@ -56,6 +57,8 @@ struct GemmArgs {
   float* out;
   // fp32 epilogue: optional bf16 residual [M][N] added to the product (null: none)
   const uint16_t* resid;
+  // gate/up epilogue: silu(gate)·up as bf16 [M][N/2]
+  uint16_t* glu_out;
 };
 
 // Chunk permutation of row r for LDS rows of KB bf16 (KB/8 chunks of 16 bytes).
@@ -92,6 +95,14 @@ __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_tok, int
   tf = r / gsz;
 }
 
+// silu(g)·u with silu(g) = g / (1 + e^-g) ("Llama 3" page, SwiGLU MLP), in
+// fp32: e^-g as 2^(-g·log2 e) (v_exp_f32); for g below about -88 the power is
+// +inf and the quotient -0, the limit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+  return g / (1.0f + e) * u;
+}
+
 // Rotation of pairs (v0, v1) and (v2, v3) by the angles whose (cos, sin) are
 // (cs[0], cs[1]) and (cs[2], cs[3]) (the 2x2 rotation display of the Rotary
 // positional encoding page: first member c*z0 - s*z1, second s*z0 + c*z1).
@@ -103,14 +114,27 @@ __device__ __forceinline__ void rotate_pairs(float& v0, float& v1, float& v2, fl
   v0 = r0; v1 = r1; v2 = r2; v3 = r3;
 }
 
-// Row f of the weight operand: for the fused QKV product (N = 6144), output
-// columns [0,4096) are W_Q rows, then W_K, then W_V; otherwise W_O rows.
+// Row f of the weight operand.
+//  * Fused QKV product (N = 6144): output columns [0,4096) are W_Q rows, then
+//    W_K, then W_V.
+//  * Gate/up product of the MLP: each wave's WPF feature rows are WPF/2 gate
+//    (w1) rows followed by the up (w3) rows of the same hidden units, so that
+//    a lane's accumulators hold both factors of silu(gate)·up. Wave block
+//    starting at feature fb covers hidden units fb/2 .. fb/2 + WPF/2 - 1.
+//  * Otherwise rows of w0.
+template <int EPI, int WPF>
 __device__ __forceinline__ const uint16_t* weight_row(const GemmArgs& a, int f) {
-  if (a.N == N_QKV) {
-    if (f >= D_MODEL + N_KV * D_HEAD) return a.w2 + (size_t)(f - D_MODEL - N_KV * D_HEAD) * D_MODEL;
-    if (f >= D_MODEL) return a.w1 + (size_t)(f - D_MODEL) * D_MODEL;
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int w = f % WPF;
+    const int unit = (f - w) / 2 + (w % (WPF / 2));
+    return (w < WPF / 2 ? a.w0 : a.w1) + (size_t)unit * a.K;
+  } else {
+    if (a.N == N_QKV) {
+      if (f >= D_MODEL + N_KV * D_HEAD) return a.w2 + (size_t)(f - D_MODEL - N_KV * D_HEAD) * a.K;
+      if (f >= D_MODEL) return a.w1 + (size_t)(f - D_MODEL) * a.K;
+    }
+    return a.w0 + (size_t)f * a.K;
   }
-  return a.w0 + (size_t)f * D_MODEL;
 }
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
@@ -119,7 +143,7 @@ struct GemmCfg {
   static constexpr int BK = KB;
   static constexpr int CPR = KB / 8;                   // 16-byte chunks per LDS row
   static constexpr int RPI = 512 / KB;                 // LDS rows per 1 KiB load instruction
-  static constexpr bool SWAP = (EPI == EPI_QKV_ROPE);
+  static constexpr bool SWAP = (EPI == EPI_QKV_ROPE || EPI == EPI_SWIGLU);
   static constexpr int PR = SWAP ? FEAT : TOK;   // MFMA A operand rows
   static constexpr int QR = SWAP ? TOK : FEAT;   // MFMA B operand rows
   static constexpr int NW = WPN * WQN;
@@ -134,6 +158,7 @@ struct GemmCfg {
   static_assert(WP % 32 == 0 && WQ % 32 == 0, "wave tile must be whole 32x32 MFMA blocks");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(EPI != EPI_SWIGLU || NP % 2 == 0, "gate/up pairs need an even feature block count");
 };
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
@@ -157,10 +182,9 @@ void gemm_nt_kernel(GemmArgs a) {
   const int n0 = tf * FEAT;
 
   // K range of this workgroup: all of it, or slice blockIdx.y of gridDim.y (split K)
-  constexpr int NK_ALL = D_MODEL / BK;
-  const int NK = NK_ALL / (int)gridDim.y;
+  const int NK = a.K / BK / (int)gridDim.y;
   const int k_first = (int)blockIdx.y * NK;
-  const uint16_t* abase = a.act + (size_t)m0 * D_MODEL;
+  const uint16_t* abase = a.act + (size_t)m0 * a.K;
   const int tok_last = a.M - m0 - 1;   // rows past it are clamped (their outputs are discarded)
 
   // This lane's source pointers for its NI_W load instructions (K offset added per step).
@@ -176,8 +200,8 @@ void gemm_nt_kernel(GemmArgs a) {
     const bool is_p = row < PR;
     const int r = is_p ? row : row - PR;
     const bool is_tok = C::SWAP ? !is_p : is_p;
-    const uint16_t* rowp = is_tok ? abase + (size_t)min(r, tok_last) * D_MODEL
-                                  : weight_row(a, n0 + r);
+    const uint16_t* rowp = is_tok ? abase + (size_t)min(r, tok_last) * a.K
+                                  : weight_row<EPI, C::WP>(a, n0 + r);
     src[j] = rowp + (size_t)k_first * BK + lc * 8;
   }
   auto issue = [&](int kt, int stage) {
@@ -264,6 +288,28 @@ void gemm_nt_kernel(GemmArgs a) {
           *reinterpret_cast<u32x2*>(drow + f) = w;
         }
       }
+    }
+  } else if (EPI == EPI_SWIGLU) {
+    // acc[i][j][4g + e]: tile feature wp*WP + 32i + 8g + 4*lhalf + e, token
+    // m0 + wq*WQ + 32j + lrow. Blocks i < NP/2 are gate rows, block i + NP/2 the
+    // up rows of the same hidden units (weight_row's order).
+    const int ld = a.N / 2;
+    const int unit0 = (n0 + wp * C::WP) / 2;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const int tok = m0 + wq * C::WQ + j * 32 + lrow;
+      if (tok >= a.M) continue;
+      uint16_t* orow = a.glu_out + (size_t)tok * ld + unit0;
+#pragma unroll
+      for (int i = 0; i < NP / 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc[i][j][4 * g + e], acc[i + NP / 2][j][4 * g + e]);
+          const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(orow + i * 32 + 8 * g + 4 * lhalf) = w;
+        }
     }
   } else {
     // acc[i][j][r]: token m0 + wp*WP + 32i + 8(r/4) + 4*lhalf + (r&3), feature n0 + wq*WQ + 32j + lrow.
@@ -364,7 +410,7 @@ static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int ksplit = 1) 
 // epilogue kernel. a.out is the final fp32 destination (out_proj) or unused.
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int KS>
 static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
-  static_assert((D_MODEL / BK) % KS == 0, "K steps must split evenly");
+  if ((a.K / BK) % KS != 0) return hipErrorInvalidValue;   // K steps must split evenly
   float* final_out = a.out;
   a.out = part;
   hipError_t e = launch_gemm<TOK, FEAT, WPN, WQN, STAGES, EPI_PARTIAL_F32>(a, s, KS);
@@ -392,7 +438,7 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
                            long long kv_rstride, float* splitk, hipStream_t s) {
   GemmArgs a{};
-  a.act = x; a.w0 = wq; a.w1 = wk; a.w2 = wv; a.M = M; a.N = N_QKV;
+  a.act = x; a.w0 = wq; a.w1 = wk; a.w2 = wv; a.M = M; a.N = N_QKV; a.K = D_MODEL;
   a.rope = rope; a.T = T;
   a.q_dst = q_dst; a.q_bstride = q_bstride; a.q_rstride = q_rstride;
   a.k_dst = k_dst; a.v_dst = v_dst; a.kv_bstride = kv_bstride; a.kv_rstride = kv_rstride;
@@ -410,7 +456,34 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
                            const uint16_t* resid, float* splitk, hipStream_t s) {
   GemmArgs a{};
-  a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.out = out; a.T = 1; a.resid = resid;
+  a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.K = D_MODEL; a.out = out; a.T = 1;
+  a.resid = resid;
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
+  if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
+  if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
+  return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+}
+size_t gemm_mlp_splitk_bytes(int M) {
+  return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * D_MODEL * sizeof(float) : 0;
+}
+
+hipError_t launch_mlp_gate_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3, int M,
+                              uint16_t* a_out, hipStream_t s) {
+  GemmArgs a{};
+  a.act = x; a.w0 = w1; a.w1 = w3; a.M = M; a.N = 2 * D_FF; a.K = D_MODEL; a.glu_out = a_out;
+  a.T = 1;
+  // 2 x 14336 features give enough workgroups at any M without splitting K
+  if (M <= 64) return launch_gemm<64, 64, 1, 2, 8, EPI_SWIGLU>(a, s);
+  if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_SWIGLU>(a, s);
+  if (M <= 8192) return launch_gemm<128, 256, 2, 2, 2, EPI_SWIGLU>(a, s);
+  return launch_gemm<256, 256, 4, 2, 2, EPI_SWIGLU>(a, s);
+}
+
+hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float* out,
+                           const uint16_t* resid, float* splitk, hipStream_t s) {
+  GemmArgs a{};
+  a.act = act; a.w0 = w2; a.M = M; a.N = D_MODEL; a.K = D_FF; a.out = out; a.T = 1;
+  a.resid = resid;
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);

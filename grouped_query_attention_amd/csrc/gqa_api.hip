@@ -77,6 +77,21 @@ inline DecodeWs decode_layout(int B, int S_max) {
   return w;
 }
 
+// SwiGLU MLP: x̂ (bf16, pre-norm form only), A = silu(gate)·up (bf16), then the
+// down product's split-reduction partials (M <= 64 tokens only).
+struct MlpWs {
+  size_t xn, a, part, total;
+};
+
+inline MlpWs mlp_layout(int M) {
+  MlpWs w{};
+  w.xn = 0;
+  w.a = align_up((size_t)M * D_MODEL * 2);
+  w.part = w.a + align_up((size_t)M * gqa::D_FF * 2);
+  w.total = w.part + align_up(gqa::gemm_mlp_splitk_bytes(M));
+  return w;
+}
+
 inline int hip_status(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
 inline bool tokens_ok(int B, int T) {
@@ -236,6 +251,34 @@ int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
   e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   return hip_status(gqa::launch_out_proj(h, w_o, B, out, norm ? x : nullptr, part, s));
+}
+
+int mlp_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w1, const gqa_bf16* w2,
+             const gqa_bf16* w3, int M, float* out, gqa_bf16* a_out, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  if (!x || !out || !w1 || !w2 || !w3) return GQA_ERR_NULL;
+  if (norm) {
+    const int st = check_prenorm(*norm);
+    if (st != GQA_OK) return st;
+  }
+  if (M < 1 || M > GQA_MAX_TOKENS) return GQA_ERR_SHAPE;
+  if (misaligned(x) || misaligned(out) || misaligned(w1) || misaligned(w2) || misaligned(w3) ||
+      (a_out && misaligned(a_out)))
+    return GQA_ERR_ALIGN;
+  const MlpWs L = mlp_layout(M);
+  if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
+  if (misaligned(workspace)) return GQA_ERR_ALIGN;
+
+  char* ws = static_cast<char*>(workspace);
+  gqa_bf16* act = a_out ? a_out : reinterpret_cast<gqa_bf16*>(ws + L.a);
+  float* part = L.total > L.part ? reinterpret_cast<float*>(ws + L.part) : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  const gqa_bf16* xin = norm_input(norm, x, M, reinterpret_cast<gqa_bf16*>(ws + L.xn), s, &e);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  e = gqa::launch_mlp_gate_up(xin, w1, w3, M, act, s);
+  if (e != hipSuccess) return GQA_ERR_HIP;
+  return hip_status(gqa::launch_mlp_down(act, w2, M, out, norm ? x : nullptr, part, s));
 }
 
 }  // namespace
@@ -439,6 +482,25 @@ int gqa_rmsnorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, gqa
   if (st != GQA_OK) return st;
   if (misaligned(x) || misaligned(y)) return GQA_ERR_ALIGN;
   return hip_status(gqa::launch_rmsnorm(x, norm_w, eps, M, y, (hipStream_t)stream));
+}
+
+size_t gqa_mlp_workspace_bytes(int M) {
+  if (M < 1 || M > GQA_MAX_TOKENS) return 0;
+  return mlp_layout(M).total;
+}
+
+int gqa_mlp_forward(const gqa_bf16* x, const gqa_bf16* w1, const gqa_bf16* w2,
+                    const gqa_bf16* w3, int M, float* out, gqa_bf16* a_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return mlp_impl(x, nullptr, w1, w2, w3, M, out, a_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_mlp_forward_prenorm(const gqa_bf16* h, const gqa_bf16* norm_w, float eps,
+                            const gqa_bf16* w1, const gqa_bf16* w2, const gqa_bf16* w3, int M,
+                            float* out, gqa_bf16* a_out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const PreNorm n{norm_w, eps};
+  return mlp_impl(h, &n, w1, w2, w3, M, out, a_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

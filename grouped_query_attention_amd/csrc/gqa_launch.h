@@ -24,6 +24,16 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
 hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* out,
                            const uint16_t* resid, float* splitk, hipStream_t s);
 
+// SwiGLU MLP: a[M][14336] (bf16) = silu(x·w1ᵀ)·(x·w3ᵀ), one fused product of
+// x[M][4096] with w1, w3 [14336][4096]; then out[M][4096] (fp32) = a·w2ᵀ
+// (w2 [4096][14336]) + resid (bf16, when not null). `splitk` (may be null) is
+// fp32 scratch of gemm_mlp_splitk_bytes(M) bytes for M <= 64 (decode).
+hipError_t launch_mlp_gate_up(const uint16_t* x, const uint16_t* w1, const uint16_t* w3, int M,
+                              uint16_t* a_out, hipStream_t s);
+hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float* out,
+                           const uint16_t* resid, float* splitk, hipStream_t s);
+size_t gemm_mlp_splitk_bytes(int M);
+
 // y[M][4096] (bf16) = RMS normalisation of x[M][4096] rows with gain w[4096].
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* w, float eps, int M, uint16_t* y,
                           hipStream_t s);

@@ -228,6 +228,33 @@ int gqa_rmsnorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps, int M, gqa
                 void* stream);
 
 /*
+ * SwiGLU MLP, the other half of the decoder block ("Llama 3" page, section
+ * "SwiGLU MLP"): three bias-free projections,
+ *     out = w2( silu(x·w1ᵀ) ⊙ (x·w3ᵀ) ),  silu(g) = g / (1 + e^-g),
+ * d_ff = 14336 (the SiLU panel's shapes). Gate and up are one product whose
+ * epilogue forms silu(gate)·up in fp32 and rounds it once to bf16 (A); the
+ * down product accumulates in fp32.
+ *   x      [M][4096]    bf16   input rows (tokens)
+ *   w1, w3 [14336][4096] bf16  gate and up projections, [out][in]
+ *   w2     [4096][14336] bf16  down projection, [out][in]
+ *   out    [M][4096]    f32    result
+ *   a_out  [M][14336]   bf16   A = silu(gate)·up, or NULL (then it stays in
+ *                              the workspace)
+ *   workspace  >= gqa_mlp_workspace_bytes(M) bytes (device)
+ * 1 <= M <= GQA_MAX_TOKENS. The _prenorm form reads RMSNorm(x) (gain norm_w
+ * [4096] bf16, eps as for gqa_block_forward_prenorm; the block's ffn_norm)
+ * and returns out = x + MLP(x̂) (Merge and project page, handoff excerpt).
+ */
+size_t gqa_mlp_workspace_bytes(int M);
+int gqa_mlp_forward(const gqa_bf16* x, const gqa_bf16* w1, const gqa_bf16* w2,
+                    const gqa_bf16* w3, int M, float* out, gqa_bf16* a_out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+int gqa_mlp_forward_prenorm(const gqa_bf16* h, const gqa_bf16* norm_w, float eps,
+                            const gqa_bf16* w1, const gqa_bf16* w2, const gqa_bf16* w3, int M,
+                            float* out, gqa_bf16* a_out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * Stage 1 alone: Q, K, V projections with the pair rotation applied to Q and K
  * ("All 13 steps": the three projections and the rotation). Each output is
  * rounded to bf16 once, after the rotation.

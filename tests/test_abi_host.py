@@ -222,3 +222,23 @@ def test_prenorm_entries_reject():
         1 << 40, None)
     assert chk(None, 1e-5) == NULL and chk(FAKE, -2.0) == ARG
     assert chk(FAKE, 1e-5, sp=9) == SHAPE
+
+
+def test_mlp_entries_reject_and_sizes():
+    lib = gqa.lib()
+    M = 300
+    need = M * 4096 * 2 + M * 14336 * 2          # x̂ and A (bf16); no split partials
+    assert gqa.mlp_workspace_bytes(M) >= need
+    assert gqa.mlp_workspace_bytes(M) < need + 1024
+    assert gqa.mlp_workspace_bytes(60) >= 60 * (4096 + 14336) * 2 + 4 * 60 * 4096 * 4
+    assert gqa.mlp_workspace_bytes(0) == 0
+    f = lambda **kw: lib.gqa_mlp_forward(kw.get("x", FAKE), kw.get("w1", FAKE), FAKE, FAKE,
+                                         kw.get("M", M), kw.get("out", FAKE), kw.get("a", None),
+                                         kw.get("ws", FAKE), kw.get("wsb", 1 << 40), None)
+    assert f(x=None) == NULL and f(w1=None) == NULL and f(out=None) == NULL
+    assert f(M=0) == SHAPE and f(M=(1 << 24) + 1) == SHAPE
+    assert f(x=MIS) == ALIGN and f(a=MIS) == ALIGN and f(ws=MIS) == ALIGN
+    assert f(ws=None) == WORKSPACE and f(wsb=gqa.mlp_workspace_bytes(M) - 1) == WORKSPACE
+    p = lambda g, eps: lib.gqa_mlp_forward_prenorm(FAKE, g, eps, FAKE, FAKE, FAKE, M, FAKE, None,
+                                                   FAKE, 1 << 40, None)
+    assert p(None, 1e-5) == NULL and p(FAKE, -1.0) == ARG and p(MIS, 1e-5) == ALIGN
