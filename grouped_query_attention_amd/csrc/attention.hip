@@ -140,17 +140,36 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   // Direct-to-LDS loads of tile t: instruction i (0..31) covers rows 4(i&15)..+3
   // of K (i < 16) or V; lane l writes row 4(i&15) + (l >> 4), physical chunk
   // l & 15. Keys past the end are clamped to the last key (finite values; masked).
+  // This lane's source for instruction j at tile 0; a whole tile adds a uniform
+  // offset, and only a tile reaching past the last key takes the clamped path.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint16_t* src0[FA_NI_W];
+#pragma unroll
+  for (int j = 0; j < FA_NI_W; ++j) {
+    const int i = wave_u + 8 * j;
+    const bool isv = i >= 16;
+    const int r = 4 * (i & 15) + (lane >> 4);
+    const int lc = isv ? ((lane & 15) ^ ((r & 3) << 2)) : ((lane & 15) ^ (r & 15));
+    src0[j] = (isv ? vbase : kbase) + (size_t)r * (N_KV * D_HEAD) + lc * 8;
+  }
   auto issue = [&](int t) {
     uint16_t* st = smem + (t % FA_STAGES) * 2 * FA_TILE;
+    if (t * FA_BN + FA_BN <= a.kv_len) {
+      const size_t toff = (size_t)t * FA_BN * (N_KV * D_HEAD);
 #pragma unroll
-    for (int j = 0; j < FA_NI_W; ++j) {
-      const int i = wave + 8 * j;
-      const bool isv = i >= 16;
-      const int r = 4 * (i & 15) + (lane >> 4);
-      const int key = min(t * FA_BN + r, a.kv_len - 1);
-      const int lc = isv ? ((lane & 15) ^ ((r & 3) << 2)) : ((lane & 15) ^ (r & 15));
-      const uint16_t* src = (isv ? vbase : kbase) + (size_t)key * (N_KV * D_HEAD) + lc * 8;
-      dma16((const void*)src, (st + (isv ? FA_TILE : 0) + (i & 15) * 512));
+      for (int j = 0; j < FA_NI_W; ++j) {
+        const int i = wave_u + 8 * j;
+        dma16((const void*)(src0[j] + toff), (st + (i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < FA_NI_W; ++j) {
+        const int i = wave_u + 8 * j;
+        const int r = 4 * (i & 15) + (lane >> 4);
+        const int key = min(t * FA_BN + r, a.kv_len - 1);
+        const uint16_t* src = src0[j] + (ptrdiff_t)(key - r) * (N_KV * D_HEAD);
+        dma16((const void*)src, (st + (i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+      }
     }
   };
 
@@ -167,20 +186,28 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   // S^T = K·Q^T, then the online softmax of tile t, leaving P^T in pf.
   auto qk_softmax = [&](int t) {
     const uint16_t* sk = smem + (t % FA_STAGES) * 2 * FA_TILE;
-    // Two partial sums per 32-key block over alternate d steps: four independent
-    // accumulation chains, so no MFMA waits on the result of the one before it.
-    f32x16 sp[2][2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) sp[kb2][0] = sp[kb2][1] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-        sp[kb2][st & 1] = mfma_32x32x16(ld16(sk + k_off(kb2 * 32 + lrow, 2 * st + lhalf)), qf[st],
-                                        sp[kb2][st & 1]);
+    // One accumulation chain per 32-key block, the two blocks interleaved. The K
+    // fragments of step st+2 are read while the MFMAs of step st run (a ring of
+    // three register buffers; the scheduling fences keep the compiler from
+    // sinking the reads next to their use).
     f32x16 s[2];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = sp[kb2][0] + sp[kb2][1];
+    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = f32x16{};
+    u32x4 kf[3][2];
+    auto read_k = [&](int st, u32x4 (&f)[2]) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) f[kb2] = ld16(sk + k_off(kb2 * 32 + lrow, 2 * st + lhalf));
+    };
+    read_k(0, kf[0]);
+    read_k(1, kf[1]);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      if (st + 2 < 8) read_k(st + 2, kf[(st + 2) % 3]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma_32x32x16(kf[st % 3][kb2], qf[st], s[kb2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // lane holds query lrow, keys 32kb + 8(i>>2) + 4*lhalf + (i&3)
     const int k0 = t * FA_BN;
     const bool edge = (a.causal && (k0 + FA_BN - 1 > a.q_pos0 + q0)) || (k0 + FA_BN > a.kv_len) || has_mask;
@@ -196,14 +223,17 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
           s[kb2][i] = x;
         }
     }
+    // Lanes l and l ^ 32 hold the two halves of a query row's keys and keep the
+    // same reference max. Each half tests its own maximum; only when some half
+    // exceeds the threshold (rare) are the halves combined and the row rescaled.
     float mx = NEG_INF;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool need = mx > m_ref + FA_RESCALE_RAW;     // false when mx = -inf
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + FA_RESCALE_RAW) != 0) {
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool need = mx > m_ref + FA_RESCALE_RAW;   // false when mx = -inf
       const float m_new = need ? mx : m_ref;
       const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2);   // 0 from -inf
       m_ref = m_new;
