@@ -432,6 +432,19 @@ size_t gemm_splitk_bytes(int M) {
   return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * N_QKV * sizeof(float) : 0;
 }
 
+// Products with 4096 fp32 output features (W_O, the MLP's down product), by M:
+// split K with a workspace at M <= 64; 128x128 tiles to M = 1024; 128-token x
+// 256-feature tiles of 8 waves to M = 4096 (one workgroup per CU at M = 2048;
+// 3-10 % faster there than 128x128); 256x256 beyond.
+static hipError_t launch_fp32_out(GemmArgs a, float* splitk, hipStream_t s) {
+  const int M = a.M;
+  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
+  if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
+  if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
+  if (M <= 4096) return launch_gemm<128, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+  return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+}
+
 hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
@@ -458,11 +471,9 @@ hipError_t launch_out_proj(const uint16_t* h, const uint16_t* wo, int M, float* 
   GemmArgs a{};
   a.act = h; a.w0 = wo; a.M = M; a.N = D_MODEL; a.K = D_MODEL; a.out = out; a.T = 1;
   a.resid = resid;
-  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
-  if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
-  if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
-  return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+  return launch_fp32_out(a, splitk, s);
 }
+
 size_t gemm_mlp_splitk_bytes(int M) {
   return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * D_MODEL * sizeof(float) : 0;
 }
@@ -487,10 +498,7 @@ hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float
   GemmArgs a{};
   a.act = act; a.w0 = w2; a.M = M; a.N = D_MODEL; a.K = D_FF; a.out = out; a.T = 1;
   a.resid = resid;
-  if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
-  if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
-  if (M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
-  return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+  return launch_fp32_out(a, splitk, s);
 }
 #endif
 
