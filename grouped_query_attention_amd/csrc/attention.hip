@@ -123,8 +123,9 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lrow = lane & 31, lhalf = lane >> 5;
   // Waves w and w+4 share a SIMD. The first four run each tile as QK -> softmax
-  // -> P·V; the other four run the P·V of the previous tile first, so on every
-  // SIMD one wave's MFMAs overlap the other's softmax between two barriers.
+  // -> P·V; the other four run the softmax and P·V of the previous tile first
+  // and the QK of this tile last, so on every SIMD one wave's softmax VALU
+  // work overlaps the other's MFMAs for most of a trip.
   const bool lag = wave >= 4;
   const int q0 = qt * FA_BQ;
   const int h = g * N_REP + (wave & 3);
@@ -183,14 +184,13 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   const bool has_mask = a.mask != nullptr;
   const float* mrow = has_mask ? a.mask + (size_t)(qi < a.T ? qi : 0) * a.kv_len : nullptr;
 
-  // S^T = K·Q^T, then the online softmax of tile t, leaving P^T in pf.
-  auto qk_softmax = [&](int t) {
+  // S^T = K·Q^T for tile t into s.
+  auto qk = [&](int t, f32x16 (&s)[2]) {
     const uint16_t* sk = smem + (t % FA_STAGES) * 2 * FA_TILE;
     // One accumulation chain per 32-key block, the two blocks interleaved. The K
     // fragments of step st+2 are read while the MFMAs of step st run (a ring of
     // three register buffers; the scheduling fences keep the compiler from
     // sinking the reads next to their use).
-    f32x16 s[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = f32x16{};
     u32x4 kf[3][2];
@@ -208,6 +208,10 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
       for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma_32x32x16(kf[st % 3][kb2], qf[st], s[kb2]);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // The online softmax of tile t from its raw scores s, leaving P^T in pf.
+  auto softmax = [&](int t, f32x16 (&s)[2]) {
     // lane holds query lrow, keys 32kb + 8(i>>2) + 4*lhalf + (i&3)
     const int k0 = t * FA_BN;
     const bool edge = (a.causal && (k0 + FA_BN - 1 > a.q_pos0 + q0)) || (k0 + FA_BN > a.kv_len) || has_mask;
@@ -310,6 +314,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   wait_vmcnt<0>();
   // trip t: tile t is computed (the lagging waves finish tile t-1); one extra
   // trip lets the lagging waves do the last P·V.
+  f32x16 s[2];
   for (int t = kt0; t <= kt1; ++t) {
     // tile t resident (tile t+1 may still be in flight); every wave is past
     // trip t-1, so stage (t+2)%4 — last read as tile t-2 — is free
@@ -317,10 +322,11 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
     barrier_no_fence();
     if (t + 2 < kt1) issue(t + 2);
     if (!lag) {
-      if (t < kt1) { qk_softmax(t); pv(t); }
+      if (t < kt1) { qk(t, s); softmax(t, s); pv(t); }
     } else {
-      if (t > kt0) pv(t - 1);
-      if (t < kt1) qk_softmax(t);
+      // softmax VALU work first, while the SIMD's leading wave runs its score MFMAs
+      if (t > kt0) { softmax(t - 1, s); pv(t - 1); }
+      if (t < kt1) qk(t, s);
     }
   }
 
