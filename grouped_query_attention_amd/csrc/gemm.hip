@@ -246,7 +246,7 @@ void gemm_nt_kernel(GemmArgs a) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       // The reads of slice kk+1 go out one at a time between the MFMAs of slice
-      // kk (scheduling groups: read, MFMA, read, MFMA, ...): a burst of reads
+      // kk (scheduling groups: MFMA, read, MFMA, read, ...): a burst of reads
       // from all eight waves queues up in the LDS; spread out they return in
       // time (QKV at M = 2048: 8 % faster than issuing them as a block).
       if (kk + 1 < BK / 16) read_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
@@ -258,8 +258,8 @@ void gemm_nt_kernel(GemmArgs a) {
       if (kk + 1 < BK / 16) {
 #pragma unroll
         for (int r = 0; r < NP + NQ; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
         }
       }
       __builtin_amdgcn_sched_barrier(0);
