@@ -203,11 +203,17 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st + 2 < 8) read_k(st + 2, kf[(st + 2) % 3]);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = mfma_32x32x16(kf[st % 3][kb2], qf[st], s[kb2]);
-      __builtin_amdgcn_sched_barrier(0);
     }
+    // order: the first two steps' reads, then MFMA, read, MFMA, read, ...
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
   };
 
   // The online softmax of tile t from its raw scores s, leaving P^T in pf.
