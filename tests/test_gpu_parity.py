@@ -181,6 +181,22 @@ def test_block_forward_c3_sampled():
         assert_close(hh[b, rows], ref["h"], rel=BLOCK_H_REL, mabs=BLOCK_H_ABS, what=f"H C3 b={b}")
 
 
+def test_block_forward_ragged_5000_sampled():
+    # M = 5000: 256x256 QKV and W_O tiles with a ragged last token tile, plain
+    # (unbalanced) causal attention over 79 query tiles with a ragged tail
+    print("[case] block_forward B=1 T=5000 seed=36 (sampled rows)", flush=True)
+    T = 5000
+    inp = gi.make_block_inputs(36, 1, T)
+    out, h = _prefill(inp, h=True)
+    rows = np.unique(np.concatenate([[0, 63, 64, 4095, 4096, 4991, T - 1],
+                                     np.random.Generator(np.random.PCG64(37)).integers(0, T, 40)]))
+    ref = O.block_forward_rows(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8, rows)
+    sel = torch.from_numpy(rows).to(dev())
+    assert_close(f32_to_np_f64(out[0, sel]), ref["delta"], what="Δ T=5000")
+    assert_close(bf16_to_np_f64(h[0, sel]).reshape(len(rows), 4096), ref["h"], rel=BLOCK_H_REL,
+                 mabs=BLOCK_H_ABS, what="H T=5000")
+
+
 def test_block_forward_c5_sampled():
     print("[case] block_forward C5 B=1 T=131072 seed=5 (sampled rows)", flush=True)
     T = 131072
