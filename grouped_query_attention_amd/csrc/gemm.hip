@@ -497,7 +497,8 @@ hipError_t launch_mlp_gate_up(const uint16_t* x, const uint16_t* w1, const uint1
   // 235 MB of w1 and w3) than a deeper ring at one workgroup per CU (57 us).
   if (M <= 64) return launch_gemm<64, 64, 1, 2, 4, EPI_SWIGLU>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_SWIGLU>(a, s);
-  if (M <= 8192) return launch_gemm<128, 256, 2, 2, 2, EPI_SWIGLU>(a, s);
+  // 2 x 14336 features leave 896 workgroups of 256x256 at M = 2048: the large
+  // tiles win there (about a fifth faster than 128x256)
   return launch_gemm<256, 256, 4, 2, 2, EPI_SWIGLU>(a, s);
 }
 
