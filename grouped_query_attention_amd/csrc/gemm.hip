@@ -507,6 +507,10 @@ hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float
   GemmArgs a{};
   a.act = act; a.w0 = w2; a.M = M; a.N = D_MODEL; a.K = D_FF; a.out = out; a.T = 1;
   a.resid = resid;
+  // K = 14336 makes every workgroup 3.5x longer than for W_O: at M = 2048 the
+  // 512 workgroups of 128x128 beat 128x256 tiles (221 vs 240 us); from M = 8192
+  // on, 256x256
+  if (M > SPLITK_MAX_M && M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
   return launch_fp32_out(a, splitk, s);
 }
 #endif
