@@ -267,34 +267,58 @@ void gemm_nt_kernel(GemmArgs a) {
   }
 
   if (EPI == EPI_QKV_ROPE) {
+    // Rotation in registers and one bf16 rounding; the rounded tile then goes
+    // through LDS (the load ring is idle after the last K step) so that the
+    // global stores are whole 16-byte chunks of token rows instead of 8-byte
+    // pieces of 32 different rows per instruction.
     // acc[i][j][4g + e]: feature n0 + wp*WP + 32i + 8g + 4*lhalf + e, token m0 + wq*WQ + 32j + lrow.
     // A 32-feature block lies inside one of Q, K, V (their bounds are multiples of 1024).
+    constexpr int CPT = FEAT / 8;                       // 16-byte chunks per tile row
+    constexpr int SWZ = CPT >= 8 ? 7 : CPT - 1;         // chunk c of row r at c ^ (r & SWZ)
+    static_assert(CPT % (SWZ + 1) == 0, "chunk swizzle stays inside the row");
+    static_assert(TOK * FEAT * 2 <= C::LDS_BYTES, "bf16 tile fits the load ring");
+    uint16_t* tile = smem;
+    __syncthreads();   // every wave is done reading the last stage
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int tok = m0 + wq * C::WQ + j * 32 + lrow;
-      if (tok >= a.M) continue;
-      const int b = tok / a.T;
-      const int t = tok - b * a.T;
+      const int tl = wq * C::WQ + j * 32 + lrow;
+      const int tok = min(m0 + tl, a.M - 1);
+      const int t = tok - (tok / a.T) * a.T;
       const float* rrow = a.rope + (size_t)t * (2 * 64);
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int fblk = n0 + wp * C::WP + i * 32;
-        const int region = fblk < D_MODEL ? 0 : (fblk < D_MODEL + N_KV * D_HEAD ? 1 : 2);
-        const int fbase = region == 0 ? 0 : (region == 1 ? D_MODEL : D_MODEL + N_KV * D_HEAD);
-        uint16_t* drow;
-        if (region == 0) drow = a.q_dst + b * a.q_bstride + t * a.q_rstride;
-        else drow = (region == 1 ? a.k_dst : a.v_dst) + b * a.kv_bstride + t * a.kv_rstride;
+        const bool rot = fblk < D_MODEL + N_KV * D_HEAD;   // Q and K rotate, V does not
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int f = fblk + 8 * g + 4 * lhalf - fbase;
+          const int f = fblk + 8 * g + 4 * lhalf;
           float v0 = acc[i][j][4 * g + 0], v1 = acc[i][j][4 * g + 1];
           float v2 = acc[i][j][4 * g + 2], v3 = acc[i][j][4 * g + 3];
-          if (region != 2)
+          if (rot)
             rotate_pairs(v0, v1, v2, v3, *reinterpret_cast<const f32x4*>(rrow + (f & (D_HEAD - 1))));
-          u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2*>(drow + f) = w;
+          const int c = (wp * C::WP + i * 32 + 8 * g) >> 3;
+          *reinterpret_cast<u32x2*>(tile + tl * FEAT + ((c ^ (tl & SWZ)) << 3) + 4 * lhalf) =
+              u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
         }
       }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < TOK * CPT; idx += C::THREADS) {
+      const int tl = idx / CPT, c = idx - tl * CPT;
+      const int tok = m0 + tl;
+      if (tok >= a.M) continue;
+      const int b = tok / a.T;
+      const int t = tok - b * a.T;
+      const int f = n0 + 8 * c;
+      uint16_t* dst;
+      if (f < D_MODEL) {
+        dst = a.q_dst + b * a.q_bstride + t * a.q_rstride + f;
+      } else {
+        const bool is_k = f < D_MODEL + N_KV * D_HEAD;
+        dst = (is_k ? a.k_dst : a.v_dst) + b * a.kv_bstride + t * a.kv_rstride +
+              (f - (is_k ? D_MODEL : D_MODEL + N_KV * D_HEAD));
+      }
+      st16(dst, ld16(tile + tl * FEAT + ((c ^ (tl & SWZ)) << 3)));
     }
   } else if (EPI == EPI_SWIGLU) {
     // acc[i][j][4g + e]: tile feature wp*WP + 32i + 8g + 4*lhalf + e, token
