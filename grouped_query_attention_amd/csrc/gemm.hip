@@ -266,7 +266,7 @@ void gemm_nt_kernel(GemmArgs a) {
     }
   }
 
-  if (EPI == EPI_QKV_ROPE) {
+  if constexpr (EPI == EPI_QKV_ROPE) {
     // Rotation in registers and one bf16 rounding; the rounded tile then goes
     // through LDS (the load ring is idle after the last K step) so that the
     // global stores are whole 16-byte chunks of token rows instead of 8-byte
@@ -320,17 +320,22 @@ void gemm_nt_kernel(GemmArgs a) {
       }
       st16(dst, ld16(tile + tl * FEAT + ((c ^ (tl & SWZ)) << 3)));
     }
-  } else if (EPI == EPI_SWIGLU) {
+  } else if constexpr (EPI == EPI_SWIGLU) {
     // acc[i][j][4g + e]: tile feature wp*WP + 32i + 8g + 4*lhalf + e, token
     // m0 + wq*WQ + 32j + lrow. Blocks i < NP/2 are gate rows, block i + NP/2 the
-    // up rows of the same hidden units (weight_row's order).
-    const int ld = a.N / 2;
-    const int unit0 = (n0 + wp * C::WP) / 2;
+    // up rows of the same hidden units (weight_row's order). silu(gate)·up is
+    // rounded once to bf16 and, as for the rotation epilogue, the tile goes
+    // through LDS to be stored as whole 16-byte chunks of token rows.
+    constexpr int UNITS = FEAT / 2;                     // hidden units per tile
+    constexpr int CPT = UNITS / 8;
+    constexpr int SWZ = CPT >= 8 ? 7 : CPT - 1;
+    static_assert(CPT % (SWZ + 1) == 0, "chunk swizzle stays inside the row");
+    static_assert(TOK * UNITS * 2 <= C::LDS_BYTES, "bf16 tile fits the load ring");
+    uint16_t* tile = smem;
+    __syncthreads();   // every wave is done reading the last stage
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const int tok = m0 + wq * C::WQ + j * 32 + lrow;
-      if (tok >= a.M) continue;
-      uint16_t* orow = a.glu_out + (size_t)tok * ld + unit0;
+      const int tl = wq * C::WQ + j * 32 + lrow;
 #pragma unroll
       for (int i = 0; i < NP / 2; ++i)
 #pragma unroll
@@ -338,9 +343,19 @@ void gemm_nt_kernel(GemmArgs a) {
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = silu_mul(acc[i][j][4 * g + e], acc[i + NP / 2][j][4 * g + e]);
-          const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>(orow + i * 32 + 8 * g + 4 * lhalf) = w;
+          const int c = (wp * C::WP / 2 + i * 32 + 8 * g) >> 3;
+          *reinterpret_cast<u32x2*>(tile + tl * UNITS + ((c ^ (tl & SWZ)) << 3) + 4 * lhalf) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
+    }
+    __syncthreads();
+    const int ld = a.N / 2;
+    for (int idx = tid; idx < TOK * CPT; idx += C::THREADS) {
+      const int tl = idx / CPT, c = idx - tl * CPT;
+      const int tok = m0 + tl;
+      if (tok >= a.M) continue;
+      st16(a.glu_out + (size_t)tok * ld + n0 / 2 + 8 * c,
+           ld16(tile + tl * UNITS + ((c ^ (tl & SWZ)) << 3)));
     }
   } else {
     // acc[i][j][r]: token m0 + wp*WP + 32i + 8(r/4) + 4*lhalf + (r&3), feature n0 + wq*WQ + 32j + lrow.
