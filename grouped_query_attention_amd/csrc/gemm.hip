@@ -5,22 +5,31 @@
 //    projection equations; weights stored [out, in] per the Query projection
 //    page), with the pair rotation of Q and K applied in the epilogue (the 2x2
 //    rotation display) before the single rounding to bf16.
-//  * out_proj: Δ = H · W_Oᵀ in fp32 (the last equation; Merge and project page).
+//  * out_proj: Δ = H · W_Oᵀ in fp32 (the last equation; Merge and project page),
+//    optionally plus a bf16 residual (the block's handoff).
+//  * The SwiGLU MLP ("Llama 3" page, SwiGLU MLP): gate and up as one product
+//    whose epilogue forms silu(gate)·up, and the down product (K = 14336)
+//    with the fp32 epilogue.
 //
-// Both are "NT" products: each operand is contiguous along the 4096-long
-// reduction axis. A workgroup computes a TOK x FEAT tile with a K step of 64.
+// All are "NT" products: each operand is contiguous along the reduction axis
+// (K = 4096, or 14336 for the MLP's down product). A workgroup computes a
+// TOK x FEAT tile with a K step of 64.
 // Operand tiles go from HBM straight into LDS (global_load_lds_dwordx4, no
 // register staging) through a ring of STAGES buffers, so STAGES-1 K steps of
 // loads are in flight while one is computed; one barrier per K step. LDS rows
 // are 128 bytes (64 bf16) with 16-byte chunk c of row r stored at c ^ rperm(r):
 // the 32x32x16 MFMA fragment reads (one chunk of 32 consecutive rows) are then
 // conflict-free, and each 64-lane load instruction still writes one
-// contiguous kilobyte of LDS as the direct-to-LDS path requires.
+// contiguous kilobyte of LDS as the direct-to-LDS path requires. Within a K
+// step each slice's fragment reads are spread between the MFMAs of the slice
+// before.
 //
-// For qkv_rope the MFMA "A" operand is the weight tile and "B" the token
-// tile, so the accumulator holds features down its rows: a lane then owns 4
-// consecutive features of one token, i.e. both members of two rotation
-// pairs, and the rotation needs no cross-lane traffic.
+// For qkv_rope (and the gate/up product) the MFMA "A" operand is the weight
+// tile and "B" the token tile, so the accumulator holds features down its
+// rows: a lane then owns 4 consecutive features of one token, i.e. both
+// members of two rotation pairs, and the rotation needs no cross-lane
+// traffic. Their bf16 results go through LDS (the idle load ring) so that the
+// global stores are whole 16-byte chunks of token rows.
 //
 // Few tokens (decode, M <= 64) make both products weight streams: every
 // weight is used by at most 64 tokens, so the time is HBM bytes, and a
