@@ -225,10 +225,13 @@ def _chunk(x_bits, inp, k_cache, v_cache, start_pos, h=False):
 
 
 # (1, 1024, 2048, 512) runs the balanced attention plan with a position offset;
-# (3, 20, 64, 44) ends exactly at S_max; (2, 1, 300, 299) is a one-position chunk
-# (split-K projections).
+# (2, 300, 1024, 700) a plan whose cut query tiles have four pieces (ragged T,
+# offset not a multiple of 64); (1, 777, 1110, 333) a shape whose plan falls
+# back to the plain launch; (3, 20, 64, 44) ends exactly at S_max;
+# (2, 1, 300, 299) is a one-position chunk (split-K projections).
 @pytest.mark.parametrize("B,T,S_max,start_pos", [(2, 37, 256, 100), (1, 128, 128, 0),
-                                                 (1, 1024, 2048, 512), (3, 20, 64, 44),
+                                                 (1, 1024, 2048, 512), (2, 300, 1024, 700),
+                                                 (1, 777, 1110, 333), (3, 20, 64, 44),
                                                  (2, 1, 300, 299)])
 def test_chunk_forward(B, T, S_max, start_pos):
     print(f"[case] chunk B={B} T={T} S_max={S_max} start_pos={start_pos}", flush=True)
