@@ -168,6 +168,7 @@ struct GemmCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
   static_assert(EPI != EPI_SWIGLU || NP % 2 == 0, "gate/up pairs need an even feature block count");
+  static constexpr bool XSTAGE = NP * NQ >= 6;         // barrier before the last slice of a step
 };
 
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
@@ -235,43 +236,81 @@ void gemm_nt_kernel(GemmArgs a) {
   // fragments double-buffered in registers: reads of slice kk+1 overlap the MFMAs
   // of kk (declared outside the step loop: the generated loop is faster)
   u32x4 af[2][NP], bf[2][NQ];
-  for (int kt = 0; kt < NK; ++kt) {
-    // wait for this step's loads; keep the later steps' loads (at most STAGES-2) in flight
-    wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 1 - kt));
-    barrier_no_fence();
-
-    const uint16_t* sp = smem + (kt % STAGES) * C::STAGE_ELEMS;
+  auto read_frags = [&](const uint16_t* sp, int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
     const uint16_t* sq = sp + PR * BK;
-    auto read_frags = [&](int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
-      const int ch = kk * 2 + lhalf;
+    const int ch = kk * 2 + lhalf;
 #pragma unroll
-      for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz<BK>(wp * C::WP + i * 32 + lrow, ch));
+    for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz<BK>(wp * C::WP + i * 32 + lrow, ch));
 #pragma unroll
-      for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 32 + lrow, ch));
-    };
-    read_frags(0, af[0], bf[0]);
-    // the next stage's loads go out while the first fragment reads are in flight
-    if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+    for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 32 + lrow, ch));
+  };
+  auto mfmas = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      // The reads of slice kk+1 go out one at a time between the MFMAs of slice
-      // kk (scheduling groups: MFMA, read, MFMA, read, ...): a burst of reads
-      // from all eight waves queues up in the LDS; spread out they return in
-      // time (QKV at M = 2048: 8 % faster than issuing them as a block).
-      if (kk + 1 < BK / 16) read_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+    for (int i = 0; i < NP; ++i)
 #pragma unroll
-      for (int i = 0; i < NP; ++i)
+      for (int j = 0; j < NQ; ++j) acc[i][j] = mfma_32x32x16(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
+  };
+  // The reads of the next slice go out one at a time between the MFMAs of this
+  // one (scheduling groups: MFMA, read, MFMA, read, ...): a burst of reads from
+  // all eight waves queues up in the LDS; spread out they return in time (QKV
+  // at M = 2048: 8 % faster than issuing them as a block).
+  auto spread = [&]() {
 #pragma unroll
-        for (int j = 0; j < NQ; ++j)
-          acc[i][j] = mfma_32x32x16(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
-      if (kk + 1 < BK / 16) {
+    for (int r = 0; r < NP + NQ; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+    }
+  };
+  constexpr int NS = BK / 16;   // MFMA slices per K step
+  if constexpr (C::XSTAGE) {
+    // The step's barrier sits before its last slice: once every wave has its
+    // last fragments in registers (lgkmcnt(0)) and the next step's loads have
+    // landed, the next step's first reads go out between the last slice's
+    // MFMAs instead of stalling the start of the next step. Used where a slice
+    // has enough MFMAs (NP * NQ >= 6) to cover those reads.
+    wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 1));
+    barrier_no_fence();
+    read_frags(smem, 0, af[0], bf[0]);
+    if (STAGES - 1 < NK) issue(STAGES - 1, (STAGES - 1) % STAGES);
+    auto body = [&](const uint16_t* sp) {
 #pragma unroll
-        for (int r = 0; r < NP + NQ; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
+      for (int kk = 0; kk < NS - 1; ++kk) {
+        read_frags(sp, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+        mfmas(kk);
+        spread();
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    for (int kt = 0; kt < NK - 1; ++kt) {
+      body(smem + (kt % STAGES) * C::STAGE_ELEMS);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters free (gfx9 encoding)
+      wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 2 - kt));
+      barrier_no_fence();
+      // every wave is done with stage kt % STAGES: refill it with step kt + STAGES
+      if (kt + STAGES < NK) issue(kt + STAGES, kt % STAGES);
+      read_frags(smem + ((kt + 1) % STAGES) * C::STAGE_ELEMS, 0, af[NS & 1], bf[NS & 1]);
+      mfmas(NS - 1);
+      spread();
       __builtin_amdgcn_sched_barrier(0);
+    }
+    body(smem + ((NK - 1) % STAGES) * C::STAGE_ELEMS);
+    mfmas(NS - 1);
+  } else {
+    for (int kt = 0; kt < NK; ++kt) {
+      // wait for this step's loads; keep the later steps' loads (at most STAGES-2) in flight
+      wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 1 - kt));
+      barrier_no_fence();
+      const uint16_t* sp = smem + (kt % STAGES) * C::STAGE_ELEMS;
+      read_frags(sp, 0, af[0], bf[0]);
+      // the next stage's loads go out while the first fragment reads are in flight
+      if (kt + STAGES - 1 < NK) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+#pragma unroll
+      for (int kk = 0; kk < NS; ++kk) {
+        if (kk + 1 < NS) read_frags(sp, kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+        mfmas(kk);
+        if (kk + 1 < NS) spread();
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 
