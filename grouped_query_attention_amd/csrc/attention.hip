@@ -90,6 +90,7 @@ constexpr int FA_MAX_BINS = 256;   // bins per (sequence, KV head)
 constexpr int FA_MAX_MERGE = 128;  // cut query tiles of a plan
 constexpr int FA_PLAN_CUS = 256;   // CUs the plan balances over (MI355X)
 constexpr int FA_MIN_PIECE = 4;    // key tiles: bins never hold fewer
+constexpr int FA_ENTRY_COST = 4;   // key-tile trips an entry costs beyond its tiles (plan balance)
 constexpr int FA_DIRECT = 255;     // slot value of an entry that writes H itself
 // Partial of one piece for one (sequence, KV head): O[4 heads][64 rows][128],
 // then max[4][64], then sum[4][64], fp32.
@@ -245,7 +246,10 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const bool need = mx > m_ref + FA_RESCALE_RAW;   // false when mx = -inf
       const float m_new = need ? mx : m_ref;
-      const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2);   // 0 from -inf
+      // lanes that keep their reference keep their sums (alpha 1: with m_ref = -inf,
+      // a row that has seen no key yet, the difference would be -inf - -inf = NaN);
+      // a first finite max gives alpha = 0 from m_ref = -inf
+      const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2) : 1.f;
       m_ref = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -485,12 +489,41 @@ bool flash_plan(int B, int T, int kv_len, int q_pos0, int causal, FlashPlan& p) 
   // (a chunk of 2048 positions after 2048 cached ones: 64 key tiles against a
   // mean of 48.5 per bin; the whole chunk step 314 -> 306 us)
   if (4 * (long long)longest * bins < 5 * U) return false;
-  // bin s holds stream units [U*s/bins, U*(s+1)/bins)
-  auto cut = [&](int s) { return (int)(U * s / bins); };
+  // Bins are filled greedily in stream order up to a cost T, where an entry
+  // costs its key tiles plus FA_ENTRY_COST (the wait for its queries and first
+  // tiles, its output write and the re-synchronisation of the waves); T is the
+  // smallest cost at which the stream fits in `bins` bins (feasibility is
+  // monotone in T, so it is found by bisection). fill returns the number of
+  // entries at cost T (recording the first `cap`: key tiles taken and bin), or
+  // -1 when the stream does not fit.
+  auto fill = [&](long long T, int cap, int* take_out, int* bin_out) -> int {
+    int qi = 0, kt = 0, n = 0;
+    for (int s = 0; s < bins && qi < nq; ++s) {
+      long long cost = 0;
+      while (qi < nq && cost + FA_ENTRY_COST + 1 <= T) {
+        const long long room = T - cost - FA_ENTRY_COST;
+        const int take = len[qi] - kt < room ? len[qi] - kt : (int)room;
+        if (n < cap) { take_out[n] = take; bin_out[n] = s; }
+        ++n;
+        cost += FA_ENTRY_COST + take;
+        kt += take;
+        if (kt == len[qi]) { ++qi; kt = 0; }
+      }
+    }
+    return qi == nq ? n : -1;
+  };
+  long long lo = (U + bins - 1) / bins, hi = U + FA_ENTRY_COST;   // one bin holds all at hi
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    if (fill(mid, 0, nullptr, nullptr) >= 0) hi = mid; else lo = mid + 1;
+  }
+  int take_of[FA_MAX_ENT], bin_of[FA_MAX_ENT];
+  const int n_ent = fill(lo, FA_MAX_ENT, take_of, bin_of);
+  if (n_ent < 0 || n_ent > FA_MAX_ENT) return false;
   // pass 1: pieces per query tile; pass 2: entries, slots, merges
   int pieces_of[256];
   for (int pass = 0; pass < 2; ++pass) {
-    int pos = 0, qi = 0, kt = 0;   // stream position; current query tile (order index), key tile
+    int qi = 0, kt = 0, n = 0;   // current query tile (order index), key tile; entry
     int next_slot[256];
     if (pass == 1) {
       p.n_slots = 0;
@@ -510,18 +543,15 @@ bool flash_plan(int B, int T, int kv_len, int q_pos0, int causal, FlashPlan& p) 
     }
     for (int s = 0; s < bins; ++s) {
       if (pass == 1) p.bin_start[s] = (unsigned short)p.n_ent;
-      const int end = cut(s + 1);
-      while (pos < end) {
-        const int take = min(end - pos, len[qi] - kt);
+      while (n < n_ent && bin_of[n] == s) {
+        const int take = take_of[n++];
         if (pass == 0) {
           ++pieces_of[qi];
         } else {
-          if (p.n_ent >= FA_MAX_ENT) return false;
           const int slot = next_slot[qi] == FA_DIRECT ? FA_DIRECT : next_slot[qi]++;
           p.ent[p.n_ent++] = (unsigned)order[qi] | (unsigned)kt << 8 |
                              (unsigned)(kt + take) << 16 | (unsigned)slot << 24;
         }
-        pos += take;
         kt += take;
         if (kt == len[qi]) { ++qi; kt = 0; }
       }
@@ -773,7 +803,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
       const bool need = mx > m_ref + FA_RESCALE_RAW;     // false when mx = -inf
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
         const float m_new = need ? mx : m_ref;
-        const float alpha = __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2);
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2) : 1.f;
         m_ref = m_new;
         l_run *= alpha;
 #pragma unroll

@@ -132,6 +132,27 @@ def test_attention_explicit_mask():
     assert_close(bf16_to_np_f64(h), want, rel=STAGE_REL, what="H (mask)")
 
 
+
+def test_attention_window_mask_rows_start_late():
+    # sliding window of 48 keys (row i sees keys i-47 .. i, -inf elsewhere): rows
+    # from 111 on have no visible key in the first key tile while their wave
+    # neighbours do, so such rows meet the lazy rescale with no reference max
+    # yet; their first tile must leave the running sums at zero, not NaN
+    B, T, W = 1, 256, 48
+    print(f"[case] attention window mask B={B} T={T} W={W}", flush=True)
+    q, k, v = _qkv_direct(413, B, T)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    mask = np.where((j <= i) & (j > i - W), 0.0, -np.inf).astype(np.float32)
+    h = gqa.attention(to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), causal=False,
+                      mask=to_dev_f32(mask))
+    torch.cuda.synchronize()
+    got = bf16_to_np_f64(h)
+    assert np.all(np.isfinite(got))
+    want = O.grouped_attention(O.bf16_to_f64(q), O.bf16_to_f64(k), O.bf16_to_f64(v),
+                               mask.astype(np.float64))
+    assert_close(got, want, rel=STAGE_REL, what="H (window mask)")
+
 # --- whole block ---------------------------------------------------------------------
 
 # (2, 30): 60 tokens take the projections' split-reduction path (M <= 64)
@@ -226,13 +247,15 @@ def _chunk(x_bits, inp, k_cache, v_cache, start_pos, h=False):
 
 # (1, 1024, 2048, 512) runs the balanced attention plan with a position offset;
 # (2, 300, 1024, 700) a plan whose cut query tiles have four pieces (ragged T,
-# offset not a multiple of 64); (1, 777, 1110, 333) a shape whose plan falls
-# back to the plain launch; (3, 20, 64, 44) ends exactly at S_max;
-# (2, 1, 300, 299) is a one-position chunk (split-K projections).
+# offset not a multiple of 64); (1, 777, 1110, 333) a plan with a ragged last
+# query tile; (1, 64, 2176, 2048) one query tile over 33 key tiles, whose plan
+# would cut it into more pieces than the merge takes and falls back to the
+# plain launch; (3, 20, 64, 44) ends exactly at S_max; (2, 1, 300, 299) is a
+# one-position chunk (split-K projections).
 @pytest.mark.parametrize("B,T,S_max,start_pos", [(2, 37, 256, 100), (1, 128, 128, 0),
                                                  (1, 1024, 2048, 512), (2, 300, 1024, 700),
-                                                 (1, 777, 1110, 333), (3, 20, 64, 44),
-                                                 (2, 1, 300, 299)])
+                                                 (1, 777, 1110, 333), (1, 64, 2176, 2048),
+                                                 (3, 20, 64, 44), (2, 1, 300, 299)])
 def test_chunk_forward(B, T, S_max, start_pos):
     print(f"[case] chunk B={B} T={T} S_max={S_max} start_pos={start_pos}", flush=True)
     inp = gi.make_block_inputs(60 + T + start_pos, B, T, cache_len=S_max)
