@@ -79,8 +79,9 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
 // launches are planned on the host, stream-K style: per (sequence, KV head)
 // the query tiles are laid out in the order last, first, second-to-last,
 // second, ... (so a long tile is followed by a short one), their key tiles are
-// concatenated, and the stream is cut into equal bins; workgroup (bin, b, g)
-// runs the pieces of its bin one after the other. A query tile cut across two
+// concatenated, and the stream is cut into bins of equal cost (key tiles plus a
+// fixed overhead per piece); workgroup (bin, b, g) runs the pieces of its bin
+// one after the other. A query tile cut across two
 // bins is computed in pieces; a piece writes an unnormalised fp32 partial
 // (O, running max, running sum) per query row, and flash_merge_kernel
 // combines the pieces of each cut tile, exactly as the online softmax
