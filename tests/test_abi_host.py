@@ -172,6 +172,18 @@ def test_chunk_workspace_sizes():
     assert gqa.chunk_workspace_bytes(1, 1024, 512) > 2 * 1024 * 4096 * 2
 
 
+
+def test_balanced_plan_partials_at_t2048():
+    # B=1 T=2048 causal: 32 query tiles of 1..32 key tiles per KV head over 32
+    # bins. The cut balances key tiles plus a fixed cost per piece, which leaves
+    # bins of (19 tiles, one piece) and (14 tiles, two pieces): 14 query tiles
+    # per KV head are cut in two, i.e. 28 partial slots of O[4][64][128] plus
+    # max and sum per row (33280 floats) for each of the 8 KV heads.
+    part = 4 * 64 * 128 + 2 * 4 * 64
+    assert gqa.attention_workspace_bytes(1, 2048, 2048, True) == 28 * 8 * part * 4
+    # many query tiles: the plain launch needs no workspace
+    assert gqa.attention_workspace_bytes(8, 4096, 4096, True) == 0
+
 def test_stage_entries_reject():
     lib = gqa.lib()
     assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, None) == SHAPE
