@@ -145,7 +145,10 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   // l & 15. Keys past the end are clamped to the last key (finite values; masked).
   // This lane's source for instruction j at tile 0; a whole tile adds a uniform
   // offset, and only a tile reaching past the last key takes the clamped path.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // the wave index as a scalar for the load addresses only: the per-lane form
+  // above keeps the lagging waves' branch the way the step loop is fastest
+  const int wave_u = wave_id();
+  const uint32_t lds0 = lds_addr(smem);
   const uint16_t* src0[FA_NI_W];
 #pragma unroll
   for (int j = 0; j < FA_NI_W; ++j) {
@@ -156,13 +159,13 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
     src0[j] = (isv ? vbase : kbase) + (size_t)r * (N_KV * D_HEAD) + lc * 8;
   }
   auto issue = [&](int t) {
-    uint16_t* st = smem + (t % FA_STAGES) * 2 * FA_TILE;
+    const uint32_t st = lds0 + 2u * (uint32_t)((t % FA_STAGES) * 2 * FA_TILE);
     if (t * FA_BN + FA_BN <= a.kv_len) {
       const size_t toff = (size_t)t * FA_BN * (N_KV * D_HEAD);
 #pragma unroll
       for (int j = 0; j < FA_NI_W; ++j) {
         const int i = wave_u + 8 * j;
-        dma16((const void*)(src0[j] + toff), (st + (i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+        dma16((const void*)(src0[j] + toff), st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     } else {
 #pragma unroll
@@ -171,7 +174,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         const int r = 4 * (i & 15) + (lane >> 4);
         const int key = min(t * FA_BN + r, a.kv_len - 1);
         const uint16_t* src = src0[j] + (ptrdiff_t)(key - r) * (N_KV * D_HEAD);
-        dma16((const void*)src, (st + (i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+        dma16((const void*)src, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     }
   };
@@ -693,8 +696,9 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
   // K/V tile ring, then two query slots (items alternate): [wave][4 heads][128]
   __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE + 2 * DC_HG * 512];
   uint16_t* const qslots = smem + DC_STAGES * 2 * DC_TILE;
+  const uint32_t lds0 = lds_addr(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int l16 = lane & 15, lg = lane >> 4;
   const int G = gridDim.x;
   // cache bases as values: selecting between fields of the argument struct per
@@ -716,13 +720,13 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
     const int bh = item / a.n_split;               // b * (8 / DC_HG) + head slice
     const int key_t = (item % a.n_split) * a.chunk + ld_t * DC_BN;
     const size_t seq = (size_t)(bh / (N_KV / DC_HG)) * a.S_max * DC_ROW + (bh % (N_KV / DC_HG)) * DC_TROW;
-    uint16_t* st = smem + stage_ld * 2 * DC_TILE;
+    const uint32_t st = lds0 + 2u * (uint32_t)(stage_ld * 2 * DC_TILE);
     if (ld_t == 0) {
       // first tile of an item: its queries go ahead of the tile, into slot ld_j & 1
       // (lane l: query head 4g + l/16, dims 8(l%16) .. +7 of this wave's KV head g)
       const int b = bh / (N_KV / DC_HG), g = (bh % (N_KV / DC_HG)) * DC_HG + w;
       dma16((const void*)(a.q + ((size_t)b * N_HEADS + g * N_REP) * D_HEAD + lane * 8),
-            qslots + ((ld_j & 1) * DC_HG + w) * 512);
+            lds0 + 2u * (uint32_t)(DC_STAGES * 2 * DC_TILE + ((ld_j & 1) * DC_HG + w) * 512));
     }
 #pragma unroll
     for (int j = 0; j < DC_NI_W; ++j) {
@@ -737,7 +741,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
       const int lc = isv ? (pc ^ ((r & 7) << 1)) : (pc ^ (r & 15));
       const int key = min(key_t + r, a.kv_len - 1);   // clamped keys are masked below
       const uint16_t* src = (isv ? vcache : kcache) + seq + (size_t)key * DC_ROW + hg * D_HEAD + lc * 8;
-      dma16((const void*)src, (st + (isv ? DC_TILE : 0) + ii * 512));
+      dma16((const void*)src, st + 2u * (uint32_t)((isv ? DC_TILE : 0) + ii * 512));
     }
     stage_ld = (stage_ld + 1) % DC_STAGES;
     if (++ld_t == ld_n) { ld_t = 0; ++ld_j; if (ld_j < my_items) ld_n = item_tiles(blockIdx.x + ld_j * G); }

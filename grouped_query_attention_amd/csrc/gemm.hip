@@ -181,7 +181,7 @@ void gemm_nt_kernel(GemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_id();
   const int wp = wave / WQN, wq = wave % WQN;
 
   const int tiles_tok = (a.M + TOK - 1) / TOK;
@@ -214,11 +214,12 @@ void gemm_nt_kernel(GemmArgs a) {
                                   : weight_row<EPI, C::WP>(a, n0 + r);
     src[j] = rowp + (size_t)k_first * BK + lc * 8;
   }
+  const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int kt, int stage) {
 #pragma unroll
     for (int j = 0; j < C::NI_W; ++j) {
       const int i = wave + j * C::NW;
-      dma16((const void*)(src[j] + kt * BK), (smem + stage * C::STAGE_ELEMS + i * 512));
+      dma16((const void*)(src[j] + kt * BK), lds0 + 2u * (uint32_t)(stage * C::STAGE_ELEMS + i * 512));
     }
   };
 
@@ -528,14 +529,15 @@ size_t gemm_splitk_bytes(int M) {
 
 // Products with 4096 fp32 output features (W_O, the MLP's down product), by M:
 // split K with a workspace at M <= 64; 128x128 tiles to M = 1024; 128-token x
-// 256-feature tiles of 8 waves to M = 4096 (one workgroup per CU at M = 2048;
-// 3-10 % faster there than 128x128); 256x256 beyond.
+// 256-feature tiles of 8 waves below M = 4096 (one workgroup per CU at M = 2048;
+// 3-10 % faster there than 128x128); 256x256 from M = 4096 (one per CU there:
+// 1121 vs 960 TFLOP/s).
 static hipError_t launch_fp32_out(GemmArgs a, float* splitk, hipStream_t s) {
   const int M = a.M;
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
-  if (M <= 4096) return launch_gemm<128, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
+  if (M < 4096) return launch_gemm<128, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
   return launch_gemm<256, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
 }
 
@@ -554,10 +556,13 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);
-  // 192-wide feature tiles give 512 workgroups at M = 2048 (256x256 tiles give
-  // 192, under one per CU); from M = 8192 on the larger tiles are faster
-  // (1040 vs 915 TFLOP/s there)
-  if (M <= 4096) return launch_gemm<128, 192, 2, 2, 2, EPI_QKV_ROPE>(a, s);
+  // 192-wide feature tiles: 256 tokens x 192 features give exactly one
+  // workgroup of 8 waves per CU at M = 2048 (4-5 % faster there and at M = 4096
+  // than two workgroups of 128 x 192 per CU); 256x256 tiles would leave 192
+  // workgroups at M = 2048. From M = 8192 on 256x256 tiles are faster (1170 vs
+  // 1080 TFLOP/s at M = 32768).
+  if (M < 2048) return launch_gemm<128, 192, 2, 2, 2, EPI_QKV_ROPE>(a, s);
+  if (M <= 4096) return launch_gemm<256, 192, 2, 4, 2, EPI_QKV_ROPE>(a, s);
   return launch_gemm<256, 256, 4, 2, 2, EPI_QKV_ROPE>(a, s);
 }
 

@@ -76,11 +76,26 @@ __device__ __forceinline__ void wait_keep(int n) {
 // draining the prefetch ring every step. The kernels issue their own waits
 // (wait_vmcnt / wait_keep) before a stage is read. M0 is written here and used
 // by nothing else in these kernels (a test checks the generated assembly).
-__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
-  const uint32_t la = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds_dst;
+// The destination is an LDS byte address (lds_addr of the __shared__ array plus
+// a byte offset) computed from wave-uniform values, so that it stays in scalar
+// registers: a destination passed as a generic pointer is converted back with a
+// null check, and one built from a per-lane wave index is moved to a scalar
+// register with v_readfirstlane, both on every load (about 8 dependent VALU and
+// SALU instructions per load in the step loops).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(la)) : "memory");
+               :: "v"(src), "s"(lds_byte) : "memory");
 }
+
+// LDS byte address of a __shared__ array (apply to the array itself: the
+// conversion of its generic address then folds to a constant).
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* shared_array) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) T*)shared_array;
+}
+
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // Workgroup barrier without the memory fence __syncthreads() carries: the
 // fence would wait for every outstanding load (vmcnt(0)), draining prefetched
