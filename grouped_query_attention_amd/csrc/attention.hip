@@ -623,7 +623,7 @@ constexpr int DC_TILE = DC_BN * DC_TROW;     // elements of one K or V tile (16 
 constexpr int DC_NI = DC_TILE / 512;         // 1-KiB loads per K or V tile
 constexpr int DC_NI_W = 2 * DC_NI / DC_HG;   // 1-KiB direct-to-LDS loads per wave per tile
 constexpr int DC_PART = N_REP * D_HEAD + 2 * N_REP;   // floats per partial: O[4][128], m[4], l[4]
-constexpr int DC_TARGET_ITEMS = 768;                  // (sequence, chunk) items per launch
+constexpr int DC_TARGET_ITEMS = 512;                  // (sequence, chunk) items per launch
 
 // Number of key chunks per sequence: enough items to balance the persistent
 // workgroups, never chunks shorter than one tile. Monotone in kv_len.
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
       const int lc = isv ? (pc ^ ((r & 7) << 1)) : (pc ^ (r & 15));
       const int key = min(key_t + r, a.kv_len - 1);   // clamped keys are masked below
       const uint16_t* src = (isv ? vcache : kcache) + seq + (size_t)key * DC_ROW + hg * D_HEAD + lc * 8;
-      dma16((const void*)src, st + 2u * (uint32_t)((isv ? DC_TILE : 0) + ii * 512));
+      dma16_nt((const void*)src, st + 2u * (uint32_t)((isv ? DC_TILE : 0) + ii * 512));
     }
     stage_ld = (stage_ld + 1) % DC_STAGES;
     if (++ld_t == ld_n) { ld_t = 0; ++ld_j; if (ld_j < my_items) ld_n = item_tiles(blockIdx.x + ld_j * G); }

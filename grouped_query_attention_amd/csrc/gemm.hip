@@ -171,13 +171,25 @@ struct GemmCfg {
   static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
   static_assert(EPI != EPI_SWIGLU || NP % 2 == 0, "gate/up pairs need an even feature block count");
   static constexpr bool XSTAGE = NP * NQ >= 12;        // barrier before the last slice of a step
+  // Waves per SIMD the workgroups that fit a CU's LDS can provide (at most 2):
+  // the register budget is sized for it (256 per wave at 2).
+  static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
+  static constexpr int MIN_WAVES_EU = (NW * WG_PER_CU + 3) / 4 >= 2 ? 2 : 1;
   static constexpr int RPM = NP * NQ / (NP + NQ) > 1 ? NP * NQ / (NP + NQ) : 1;   // MFMAs per spread read
+  // Tiles of 64 tokens serve M <= 64 (decode), a single token tile: every weight
+  // row is read by exactly one workgroup, once, so those loads stream past the
+  // caches (non-temporal). Load instruction j of every wave fills P rows iff
+  // j < NJ_P (P rows come first and split evenly over the waves).
+  static constexpr bool NT_W = TOK == 64;
+  static constexpr int NJ_P = PR / RPI / NW;
+  static_assert(!NT_W || (PR / RPI) % NW == 0, "weight loads must be whole instructions of every wave");
 };
 
-// Two waves per SIMD at least (256 registers each): eight-wave workgroups need
-// it, and four-wave ones then fit two workgroups per CU.
+// Registers for two waves per SIMD where the LDS admits them: eight-wave
+// workgroups need it, and four-wave ones then fit two workgroups per CU.
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
-__global__ __launch_bounds__(64 * WPN * WQN) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * WPN * WQN)
+__attribute__((amdgpu_waves_per_eu(GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>::MIN_WAVES_EU)))
 void gemm_nt_kernel(GemmArgs a) {
   using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>;
   constexpr int PR = C::PR, QR = C::QR, NP = C::NP, NQ = C::NQ;
@@ -224,7 +236,9 @@ void gemm_nt_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < C::NI_W; ++j) {
       const int i = wave + j * C::NW;
-      dma16((const void*)(src[j] + kt * BK), lds0 + 2u * (uint32_t)(stage * C::STAGE_ELEMS + i * 512));
+      const uint32_t dst = lds0 + 2u * (uint32_t)(stage * C::STAGE_ELEMS + i * 512);
+      if (C::NT_W && (j < C::NJ_P) == C::SWAP) dma16_nt((const void*)(src[j] + kt * BK), dst);   // weight rows
+      else dma16((const void*)(src[j] + kt * BK), dst);
     }
   };
 
