@@ -175,7 +175,11 @@ struct GemmCfg {
   // the register budget is sized for it (256 per wave at 2).
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
   static constexpr int MIN_WAVES_EU = (NW * WG_PER_CU + 3) / 4 >= 2 ? 2 : 1;
+#ifdef GQA_GEMM_RPM
+  static constexpr int RPM = GQA_GEMM_RPM;   // build-time override (tuning sweeps)
+#else
   static constexpr int RPM = NP * NQ / (NP + NQ) > 1 ? NP * NQ / (NP + NQ) : 1;   // MFMAs per spread read
+#endif
   // Tiles of 64 tokens serve M <= 64 (decode), a single token tile: every weight
   // row is read by exactly one workgroup, once, so those loads stream past the
   // caches (non-temporal). Load instruction j of every wave fills P rows iff
