@@ -62,7 +62,33 @@ def test_qkv_rope_stage(B, T):
     assert_close(bf16_to_np_f64(v), ref["v"], rel=STAGE_REL, what="V")
 
 
-@pytest.mark.parametrize("M", [1, 300, 1024])
+@pytest.mark.parametrize("T", [2048, 3000, 4096])
+def test_qkv_rope_stage_wide_tiles_sampled(T):
+    # 2048 <= M <= 4096 runs 256-token x 192-feature tiles; T = 3000 leaves a
+    # ragged last token tile. The oracle projects and rotates sampled rows only
+    # (tile edges included); every feature column of those rows is compared.
+    print(f"[case] qkv_rope wide tiles B=1 T={T} (sampled rows)", flush=True)
+    inp = gi.make_block_inputs(200 + T, 1, T)
+    x = to_dev_bf16(inp.x)
+    wq, wk, wv, _ = _weights(inp)
+    q_r, k_r, v = gqa.qkv_rope(x, wq, wk, wv, _rope(T))
+    torch.cuda.synchronize()
+    edges = [0, 255, 256, 2047, T - 257, T - 256, T - 1]
+    rows = np.unique(np.concatenate([edges, np.random.Generator(np.random.PCG64(T)).integers(0, T, 24)]))
+    xr = O.bf16_to_f64(inp.x[0, rows])
+    cos, sin = O.rope_cos_sin(rows, 128)
+    want_q = O.rope_rotate(O.split_heads(O.project(xr, O.bf16_to_f64(inp.wq)), 32)[None], cos, sin)[0]
+    want_k = O.rope_rotate(O.split_heads(O.project(xr, O.bf16_to_f64(inp.wk)), 8)[None], cos, sin)[0]
+    want_v = O.split_heads(O.project(xr, O.bf16_to_f64(inp.wv)), 8)
+    sel = torch.from_numpy(rows).to(dev())
+    assert_close(bf16_to_np_f64(q_r[0, sel]), want_q, rel=STAGE_REL, what=f"Q_r T={T}")
+    assert_close(bf16_to_np_f64(k_r[0, sel]), want_k, rel=STAGE_REL, what=f"K_r T={T}")
+    assert_close(bf16_to_np_f64(v[0, sel]), want_v, rel=STAGE_REL, what=f"V T={T}")
+
+
+# M = 3000: 128x256 tiles with a ragged last token tile; 4096 and 4100: 256x256
+# tiles (the second with a ragged last tile)
+@pytest.mark.parametrize("M", [1, 300, 1024, 3000, 4096, 4100])
 def test_output_projection_stage(M):
     print(f"[case] out_proj M={M}", flush=True)
     rng = np.random.Generator(np.random.PCG64(7 + M))
