@@ -92,9 +92,9 @@ __device__ __forceinline__ int swz(int r, int c) { return r * KB + ((c ^ rperm<K
 // XCD owns a contiguous run of tiles, and runs are walked in groups of
 // GROUP token tiles so concurrently resident tiles share operand rows in
 // that XCD's L2.
+template <int GROUP>
 __device__ __forceinline__ void tile_coords(int bid, int nwg, int tiles_tok, int tiles_feat,
                                             int& tt, int& tf) {
-  constexpr int GROUP = 8;
   int lin = bid;
   if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
   int per_group = GROUP * tiles_feat;
@@ -175,6 +175,17 @@ struct GemmCfg {
   // the register budget is sized for it (256 per wave at 2).
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
   static constexpr int MIN_WAVES_EU = (NW * WG_PER_CU + 3) / 4 >= 2 ? 2 : 1;
+  // Token tiles per group of tile_coords: an XCD's run of 32 tiles is GROUP
+  // token tiles x 32/GROUP feature tiles, and it fetches GROUP*TOK + (32/GROUP)*FEAT
+  // operand rows past its L2; GROUP = 8 minimises that for FEAT >= 1.5 TOK
+  // (128x256: W_O at M = 2048 fetches 134 instead of 168 MB), 4 otherwise
+  // (256x192: QKV fetches 172 instead of 192 MB; 256x256 at M = 32768 1-2 %
+  // faster than with 8).
+#ifdef GQA_GEMM_GROUP
+  static constexpr int GROUP = GQA_GEMM_GROUP;   // build-time override (tuning sweeps)
+#else
+  static constexpr int GROUP = 2 * FEAT >= 3 * TOK ? 8 : 4;
+#endif
 #ifdef GQA_GEMM_RPM
   static constexpr int RPM = GQA_GEMM_RPM;   // build-time override (tuning sweeps)
 #else
@@ -208,7 +219,7 @@ void gemm_nt_kernel(GemmArgs a) {
   const int tiles_tok = (a.M + TOK - 1) / TOK;
   const int tiles_feat = a.N / FEAT;
   int tt, tf;
-  tile_coords(blockIdx.x, gridDim.x, tiles_tok, tiles_feat, tt, tf);
+  tile_coords<C::GROUP>(blockIdx.x, gridDim.x, tiles_tok, tiles_feat, tt, tf);
   const int m0 = tt * TOK;
   const int n0 = tf * FEAT;
 
