@@ -70,6 +70,8 @@ struct GemmArgs {
   const uint16_t* resid;
   // gate/up epilogue: silu(gate)·up as bf16 [M][N/2]
   uint16_t* glu_out;
+  // this launch covers output features n_off .. n_off + n_len - 1 (n_len = 0: all N)
+  int n_off, n_len;
 };
 
 // Chunk permutation of row r for LDS rows of KB bf16 (KB/8 chunks of 16 bytes).
@@ -217,11 +219,11 @@ void gemm_nt_kernel(GemmArgs a) {
   const int wp = wave / WQN, wq = wave % WQN;
 
   const int tiles_tok = (a.M + TOK - 1) / TOK;
-  const int tiles_feat = a.N / FEAT;
+  const int tiles_feat = (a.n_len > 0 ? a.n_len : a.N) / FEAT;
   int tt, tf;
   tile_coords<C::GROUP>(blockIdx.x, gridDim.x, tiles_tok, tiles_feat, tt, tf);
   const int m0 = tt * TOK;
-  const int n0 = tf * FEAT;
+  const int n0 = a.n_off + tf * FEAT;
 
   // K range of this workgroup: all of it, or slice blockIdx.y of gridDim.y (split K)
   const int NK = a.K / BK / (int)gridDim.y;
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(256) void splitk_out_kernel(GemmArgs a, float* out)
 template <int TOK, int FEAT, int WPN, int WQN, int STAGES, int EPI, int KB = BK>
 static hipError_t launch_gemm(const GemmArgs& a, hipStream_t s, int ksplit = 1) {
   using C = GemmCfg<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>;
-  const int tiles = ((a.M + TOK - 1) / TOK) * (a.N / FEAT);
+  const int tiles = ((a.M + TOK - 1) / TOK) * ((a.n_len > 0 ? a.n_len : a.N) / FEAT);
   hipLaunchKernelGGL((gemm_nt_kernel<TOK, FEAT, WPN, WQN, STAGES, EPI, KB>), dim3(tiles, ksplit),
                      dim3(C::THREADS), 0, s, a);
   return hipGetLastError();
@@ -550,6 +552,7 @@ static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
 #ifndef GQA_GEMM_NO_LAUNCHERS
 constexpr int SPLITK_MAX_M = 64;
 constexpr int SPLITK = 4;
+constexpr int GEMM_CUS = 256;   // CUs a launch is sized for (MI355X)
 
 size_t gemm_splitk_bytes(int M) {
   return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * N_QKV * sizeof(float) : 0;
@@ -617,9 +620,24 @@ hipError_t launch_mlp_gate_up(const uint16_t* x, const uint16_t* w1, const uint1
   // 235 MB of w1 and w3) than a deeper ring at one workgroup per CU (57 us).
   if (M <= 64) return launch_gemm<64, 64, 1, 2, 4, EPI_SWIGLU>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_SWIGLU>(a, s);
-  // 2 x 14336 features leave 896 workgroups of 256x256 at M = 2048: the large
-  // tiles win there (about a fifth faster than 128x256)
-  return launch_gemm<256, 256, 4, 2, 2, EPI_SWIGLU>(a, s);
+  // 256x256 tiles (about a fifth faster than 128x256 at M = 2048). Their
+  // 112 feature tiles per token tile would leave a last, partial round of
+  // workgroups on the CUs (896 tiles at M = 2048: 3.5 rounds on 256 CUs, the
+  // last one on half of them); the features that do not make whole rounds go
+  // to a second launch of 256x128 tiles, twice as many workgroups of half
+  // the work.
+  const int tok_tiles = (M + 255) / 256;
+  int full = 112;
+  if (tok_tiles * 112 > GEMM_CUS) {
+    full = (tok_tiles * 112 / GEMM_CUS) * GEMM_CUS / tok_tiles;
+    if (full * tok_tiles % GEMM_CUS != 0) full = 112;   // whole rounds only
+  }
+  if (full == 112) return launch_gemm<256, 256, 4, 2, 2, EPI_SWIGLU>(a, s);
+  a.n_off = 0; a.n_len = full * 256;
+  hipError_t e = launch_gemm<256, 256, 4, 2, 2, EPI_SWIGLU>(a, s);
+  if (e != hipSuccess) return e;
+  a.n_off = full * 256; a.n_len = 2 * D_FF - full * 256;
+  return launch_gemm<256, 128, 2, 4, 2, EPI_SWIGLU>(a, s);
 }
 
 hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float* out,

@@ -69,19 +69,30 @@ def test_mlp_forward(M):
     assert np.all(err <= 2.0 ** -8 * np.abs(ref["a"]) + 1e-3)
 
 
-def test_mlp_forward_large_sampled_rows():
-    # M = 9000 takes the 256x256 gate/up tiles and 256x256 down tiles
-    M = 9000
+# M = 9000 takes the 256x256 gate/up tiles in one launch (36 token tiles x 112
+# feature tiles make no whole number of rounds on 256 CUs) and 256x256 down
+# tiles; M = 2048 and 2000 (8 token tiles, the last ragged at 2000) split the
+# gate/up product into 768 tiles of 256x256 (hidden units 0 .. 12287) and 256
+# of 256x128 (12288 .. 14335). The hidden activation A is compared as well.
+@pytest.mark.parametrize("M", [9000, 2048, 2000])
+def test_mlp_forward_large_sampled_rows(M):
     print(f"[case] mlp M={M} (sampled rows)", flush=True)
     w, (w1, w2, w3) = _weights()
-    xb = _x(1999, M)
-    out = gqa.mlp_forward(to_dev_bf16(xb), w1, w2, w3)
+    xb = _x(1999 + M, M)
+    a_out = torch.empty((M, 14336), dtype=torch.bfloat16, device=dev())
+    out = gqa.mlp_forward(to_dev_bf16(xb), w1, w2, w3, a_out=a_out)
     torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 8191, 8192, M - 1],
-                                     np.random.Generator(np.random.PCG64(5)).integers(0, M, 40)]))
-    got = f32_to_np_f64(out[torch.from_numpy(rows).to(dev())])
+    edges = [0, 1, 255, 256, 1791, 1792, M - 1] + ([8191, 8192] if M > 8192 else [])
+    rows = np.unique(np.concatenate([edges, np.random.Generator(np.random.PCG64(5)).integers(0, M, 40)]))
+    sel = torch.from_numpy(rows).to(dev())
     ref = O.mlp_forward(xb[rows], w.w1, w.w2, w.w3)
-    _close(got, ref["delta"], "MLP out sampled rows")
+    _close(f32_to_np_f64(out[sel]), ref["delta"], f"MLP out sampled rows M={M}")
+    # A is rounded to bf16 once: at most one bf16 ulp of the largest value off
+    got_a = bf16_to_np_f64(a_out[sel])
+    for lo, hi in ((0, 12288), (12288, 14336)):
+        want_a = ref["a"][:, lo:hi]
+        assert_close(got_a[:, lo:hi], want_a, mabs=float(np.abs(want_a).max()) * 2.0 ** -7,
+                     what=f"MLP A units {lo}..{hi - 1} M={M}")
 
 
 @pytest.mark.parametrize("M", [7, 64, 700])
