@@ -102,6 +102,19 @@ def test_workspace_sizes():
     assert gqa.decode_workspace_bytes(0, 10) == 0
 
 
+def test_decode_plan_512_items():
+    # The split-KV launch plans 512 (sequence, head half, key chunk) items (two
+    # per CU): 256 chunks per sequence at B = 1, 128 at B = 2, one chunk when
+    # the cache is a single 16-key tile. The workspace holds the larger of the
+    # attention partials (O[4][128], max[4], sum[4] fp32 per KV head and chunk)
+    # and the projections' split-K partials (4 x B x 6144 fp32), which share it.
+    part = 8 * (4 * 128 + 8) * 4
+    for B, chunks in ((1, 256), (2, 128)):
+        small = max(B * part, 4 * B * 6144 * 4)
+        assert (gqa.decode_workspace_bytes(B, 8192) - gqa.decode_workspace_bytes(B, 16)
+                == B * chunks * part - small)
+
+
 def _fwd(**kw):
     a = dict(x=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, wo=FAKE, rope=FAKE, mask=None, causal=1,
              B=1, T=128, kv=128, out=FAKE, h=None, ws=FAKE, wsb=1 << 40, stream=None)
