@@ -172,7 +172,9 @@ struct GemmCfg {
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
   static_assert(STAGES >= 2 && NI_W * (STAGES - 2) < 64, "vmcnt range");
   static_assert(EPI != EPI_SWIGLU || NP % 2 == 0, "gate/up pairs need an even feature block count");
-  static constexpr bool XSTAGE = NP * NQ >= 12;        // barrier before the last slice of a step
+  // barrier before the last slice of a step; its register double-buffering
+  // needs an even number of 32-wide slices per step (K step 64)
+  static constexpr bool XSTAGE = NP * NQ >= 12 && KB == 64;
   // Waves per SIMD the workgroups that fit a CU's LDS can provide (at most 2):
   // the register budget is sized for it (256 per wave at 2).
   static constexpr int WG_PER_CU = (160 * 1024) / LDS_BYTES;
@@ -299,6 +301,7 @@ void gemm_nt_kernel(GemmArgs a) {
     }
   };
   constexpr int NS = BK / 32;   // MFMA slices per K step
+  static_assert(!C::XSTAGE || NS % 2 == 0, "slice parity of the register buffers");
   if constexpr (C::XSTAGE) {
     // The step's barrier sits before its last slice: once every wave has its
     // last fragments in registers (lgkmcnt(0)) and the next step's loads have
