@@ -77,3 +77,36 @@ def test_graph_replay_decode_forward():
     ws = torch.empty(gqa.decode_workspace_bytes(B, S_max), dtype=torch.uint8, device=dev())
     _check_replays(lambda: gqa.decode_forward(x, *w, rope, kc, vc, sp, out=out, workspace=ws),
                    [out])
+
+
+def test_graph_replay_mlp_split_launch():
+    # M = 2048: the gate/up product runs as two launches (three whole rounds of
+    # 256x256 tiles, then the last 4096 features on 256x128 tiles) before the
+    # down product; the hidden activation is an output too
+    M = 2048
+    print(f"[case] graph replay mlp_forward M={M}", flush=True)
+    m = gi.make_mlp_inputs(51, M)
+    x = to_dev_bf16(m.x)
+    w1, w2, w3 = (to_dev_bf16(a) for a in (m.w1, m.w2, m.w3))
+    out = torch.empty((M, 4096), dtype=torch.float32, device=dev())
+    act = torch.empty((M, 14336), dtype=torch.bfloat16, device=dev())
+    ws = torch.empty(max(1, gqa.mlp_workspace_bytes(M)), dtype=torch.uint8, device=dev())
+    _check_replays(lambda: gqa.mlp_forward(x, w1, w2, w3, out=out, a_out=act, workspace=ws),
+                   [out, act])
+
+
+def test_graph_replay_chunk_forward():
+    # 2048 new positions after 2048 cached ones: projections with the cache
+    # write (the same values on every replay), the balanced attention plan and
+    # its merge, W_O
+    B, T, S_max, sp = 1, 2048, 4096, 2048
+    print(f"[case] graph replay chunk_forward B={B} T={T} start_pos={sp}", flush=True)
+    inp = gi.make_block_inputs(52, B, T, cache_len=S_max)
+    x = to_dev_bf16(inp.x)
+    w = [to_dev_bf16(m) for m in (inp.wq, inp.wk, inp.wv, inp.wo)]
+    kc, vc = to_dev_bf16(inp.k_cache), to_dev_bf16(inp.v_cache)
+    rope = to_dev_f32(gqa.rope_table(np.arange(sp, sp + T)))
+    out = torch.empty((B, T, 4096), dtype=torch.float32, device=dev())
+    ws = torch.empty(max(1, gqa.chunk_workspace_bytes(B, T, sp)), dtype=torch.uint8, device=dev())
+    _check_replays(lambda: gqa.chunk_forward(x, *w, rope, kc, vc, sp, out=out, workspace=ws),
+                   [out])
