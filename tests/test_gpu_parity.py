@@ -379,6 +379,23 @@ def test_decode_attention_stage(kv_len):
     assert_close(bf16_to_np_f64(h), want, rel=STAGE_REL, what="H decode stage")
 
 
+@pytest.mark.parametrize("kv_len", [65536, 65000])
+def test_decode_attention_long_context(kv_len):
+    # one sequence over a long cache: the launch plans 256 key chunks of 256
+    # keys (two head halves each, 512 items); 65000 leaves a short last chunk
+    print(f"[case] decode_attention B=1 kv_len={kv_len}", flush=True)
+    B, S = 1, 65536
+    rng = np.random.Generator(np.random.PCG64(900 + kv_len))
+    q = gi.normal_bf16(rng, (B, 32, 128), 1.28)
+    kc = gi.normal_bf16(rng, (B, S, 8, 128), 1.28)
+    vc = gi.normal_bf16(rng, (B, S, 8, 128), 1.28)
+    h = gqa.decode_attention(to_dev_bf16(q), to_dev_bf16(kc), to_dev_bf16(vc), kv_len)
+    torch.cuda.synchronize()
+    want = O.grouped_attention(O.bf16_to_f64(q)[:, None], O.bf16_to_f64(kc)[:, :kv_len],
+                               O.bf16_to_f64(vc)[:, :kv_len], None)[:, 0]
+    assert_close(bf16_to_np_f64(h), want, rel=STAGE_REL, what=f"H decode B=1 kv_len={kv_len}")
+
+
 def test_decode_matches_prefill_row():
     print("[case] decode vs prefill row p=300", flush=True)
     p = 300
