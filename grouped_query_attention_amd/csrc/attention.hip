@@ -22,11 +22,13 @@
 // happens once, at the end, in fp32.
 //
 // Decode (decode_splitkv_kernel + decode_merge_kernel): the key range of each
-// sequence is split into chunks; persistent workgroups of 8 waves (one per KV
-// head) stream whole cache rows of their chunks through LDS and write one
-// unnormalised partial (max, sum, O[4][128]) per (chunk, KV head); the merge
-// kernel rescales and sums the partials.
+// sequence is split into chunks; persistent workgroups of 4 waves (one per KV
+// head of a half of the 8) stream their chunks' cache rows through LDS and
+// write one unnormalised partial (max, sum, O[4][128]) per (chunk, KV head);
+// the merge kernel rescales and sums the partials. The launch plan is in
+// decode_plan.h.
 
+#include "decode_plan.h"
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -607,31 +609,15 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
 // Decode
 // ----------------------------------------------------------------------------
 
-constexpr int DC_BN = 16;        // keys per staged tile
-#ifndef GQA_DECODE_HEADS
-#define GQA_DECODE_HEADS 4
-#endif
-constexpr int DC_HG = GQA_DECODE_HEADS;   // KV heads per workgroup (a slice of each 2 KiB cache row)
 constexpr int DC_THREADS = 64 * DC_HG;   // wave w handles KV head DC_HG * slice + w
-#ifndef GQA_DECODE_STAGES
-#define GQA_DECODE_STAGES (16 / GQA_DECODE_HEADS)
-#endif
-constexpr int DC_STAGES = GQA_DECODE_STAGES;   // tiles in the LDS ring
 constexpr int DC_ROW = N_KV * D_HEAD;        // 1024 elements per cache row
 constexpr int DC_TROW = DC_HG * D_HEAD;      // elements per tile row (the workgroup's heads)
 constexpr int DC_TILE = DC_BN * DC_TROW;     // elements of one K or V tile (16 KiB)
 constexpr int DC_NI = DC_TILE / 512;         // 1-KiB loads per K or V tile
 constexpr int DC_NI_W = 2 * DC_NI / DC_HG;   // 1-KiB direct-to-LDS loads per wave per tile
 constexpr int DC_PART = N_REP * D_HEAD + 2 * N_REP;   // floats per partial: O[4][128], m[4], l[4]
-constexpr int DC_TARGET_ITEMS = 512;                  // (sequence, chunk) items per launch
-
-// Number of key chunks per sequence: enough items to balance the persistent
-// workgroups, never chunks shorter than one tile. Monotone in kv_len.
-__host__ __device__ inline int decode_n_split(int B, int kv_len) {
-  const int tiles = (kv_len + DC_BN - 1) / DC_BN;
-  const int want = (DC_TARGET_ITEMS + B * (N_KV / DC_HG) - 1) / (B * (N_KV / DC_HG));
-  return want < 1 ? 1 : (want > tiles ? tiles : want);
-}
+constexpr int DC_QSLOT = DC_HG * 512;        // elements of one query slot: [wave][4 heads][128]
+static_assert((DC_STAGES * 2 * DC_TILE + DC_QSLOTS * DC_QSLOT) * 2 <= 160 * 1024, "LDS budget");
 
 // Tile layout: [16 keys][4 heads][128 d]: each load reads 1 KiB of contiguous
 // cache row (the workgroup's 4 heads). Inside each head's 256 bytes, K chunk c of
@@ -682,19 +668,20 @@ __device__ __forceinline__ void decode_merge_dims(const DecodeArgs& a, int b, in
                                         pack_bf16x2(acc[6] * r, acc[7] * r)};
 }
 
-// Persistent split-KV decode. Item j = (sequence b, chunk sp) covers keys
-// [sp*chunk, min(kv_len, (sp+1)*chunk)) of all 8 KV heads. Workgroup w takes
-// items w, w+G, w+2G, ... and streams their 16-key tiles of whole cache rows
-// HBM -> LDS as one continuous sequence (the next tile always loading while one
-// is computed, across item boundaries). Wave g owns KV head g and its 4 query
-// heads: scores S^T[16 keys][16 columns] from 16x16x32 MFMAs whose columns are
-// the 4 query heads (the other 12 are zero), so a lane of the accumulator holds
-// 4 keys of one head — exactly the P^T operand of the 16x16x16 P·V MFMA, whose
-// V^T operand is one transposed LDS read. Online softmax with a lazily moved
-// reference max; each wave writes an unnormalised fp32 partial per item.
+// Persistent split-KV decode. Item = (sequence b, head half hh, chunk sp)
+// covers keys [sp*chunk, min(kv_len, (sp+1)*chunk)) of KV heads 4hh .. 4hh+3.
+// Workgroup w takes items w, w+G, w+2G, ... and streams their 16-key tiles of
+// those heads' cache-row slices HBM -> LDS as one continuous sequence (the
+// next tiles always loading while one is computed, across item boundaries).
+// Wave w owns KV head 4hh + w and its 4 query heads: scores S^T[16 keys][16
+// columns] from 16x16x32 MFMAs whose columns are the 4 query heads (the other
+// 12 are zero), so a lane of the accumulator holds 4 keys of one head —
+// exactly the P^T operand of the 16x16x16 P·V MFMA, whose V^T operand is one
+// transposed LDS read. Online softmax with a lazily moved reference max; each
+// wave writes an unnormalised fp32 partial per item.
 __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a) {
-  // K/V tile ring, then two query slots (items alternate): [wave][4 heads][128]
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE + 2 * DC_HG * 512];
+  // K/V tile ring, then DC_QSLOTS query slots (item ordinal j uses slot j % DC_QSLOTS)
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[DC_STAGES * 2 * DC_TILE + DC_QSLOTS * DC_QSLOT];
   uint16_t* const qslots = smem + DC_STAGES * 2 * DC_TILE;
   const uint32_t lds0 = lds_addr(smem);
 
@@ -722,11 +709,13 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
     const size_t seq = (size_t)(bh / (N_KV / DC_HG)) * a.S_max * DC_ROW + (bh % (N_KV / DC_HG)) * DC_TROW;
     const uint32_t st = lds0 + 2u * (uint32_t)(stage_ld * 2 * DC_TILE);
     if (ld_t == 0) {
-      // first tile of an item: its queries go ahead of the tile, into slot ld_j & 1
-      // (lane l: query head 4g + l/16, dims 8(l%16) .. +7 of this wave's KV head g)
+      // first tile of an item: its queries go ahead of the tile, into slot
+      // ld_j % DC_QSLOTS (lane l: query head 4g + l/16, dims 8(l%16) .. +7 of this
+      // wave's KV head g); no later item can refill that slot before it is read
+      // (decode_plan.h)
       const int b = bh / (N_KV / DC_HG), g = (bh % (N_KV / DC_HG)) * DC_HG + w;
       dma16((const void*)(a.q + ((size_t)b * N_HEADS + g * N_REP) * D_HEAD + lane * 8),
-            lds0 + 2u * (uint32_t)(DC_STAGES * 2 * DC_TILE + ((ld_j & 1) * DC_HG + w) * 512));
+            lds0 + 2u * (uint32_t)(DC_STAGES * 2 * DC_TILE + (ld_j % DC_QSLOTS) * DC_QSLOT + w * 512));
     }
 #pragma unroll
     for (int j = 0; j < DC_NI_W; ++j) {
@@ -779,7 +768,7 @@ __global__ __launch_bounds__(DC_THREADS) void decode_splitkv_kernel(DecodeArgs a
       wait_keep<DC_NI_W, DC_STAGES - 2>(min(DC_STAGES - 2, issued - done - 1));
       barrier_no_fence();
       if (t == 0) {
-        const uint16_t* qrow = qslots + ((j & 1) * DC_HG + w) * 512 + (l16 & 3) * D_HEAD + 8 * lg;
+        const uint16_t* qrow = qslots + (j % DC_QSLOTS) * DC_QSLOT + w * 512 + (l16 & 3) * D_HEAD + 8 * lg;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const u32x4 z = {0u, 0u, 0u, 0u};
@@ -854,30 +843,24 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 }
 
 size_t decode_partials_bytes(int B, int S_max) {
-  return (size_t)B * N_KV * decode_n_split(B, S_max) * DC_PART * sizeof(float);
+  return (size_t)B * N_KV * decode_n_split(B, S_max, N_KV) * DC_PART * sizeof(float);
 }
 
 hipError_t launch_decode_attention(const uint16_t* q_r, const uint16_t* k_cache,
                                    const uint16_t* v_cache, int B, int S_max, int kv_len,
                                    float* partials, uint16_t* h_out, hipStream_t s) {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n_cu <= 0)
-      n_cu = 256;
-  }
+  // CUs of the current device, asked on every call (no state kept between calls)
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n_cu <= 0)
+    return hipErrorInvalidDevice;
+  const DecodePlan p = decode_plan(B, kv_len, N_KV, n_cu);
   DecodeArgs a{};
   a.q = q_r; a.kc = k_cache; a.vc = v_cache; a.part = partials; a.h = h_out;
   a.B = B; a.S_max = S_max; a.kv_len = kv_len;
-  a.n_split = decode_n_split(B, kv_len);
-  const int tiles = (kv_len + DC_BN - 1) / DC_BN;
-  a.chunk = ((tiles + a.n_split - 1) / a.n_split) * DC_BN;
-  a.n_split = (kv_len + a.chunk - 1) / a.chunk;        // drop empty chunks
-  a.n_items = B * (N_KV / DC_HG) * a.n_split;
-  const int grid = a.n_items < n_cu ? a.n_items : n_cu;
-  hipLaunchKernelGGL(decode_splitkv_kernel, dim3((unsigned)grid), dim3(DC_THREADS), 0, s, a);
+  a.n_split = p.n_split; a.chunk = p.chunk; a.n_items = p.n_items;
+  hipLaunchKernelGGL(decode_splitkv_kernel, dim3((unsigned)p.grid), dim3(DC_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)(B * N_KV)), dim3(64), 0, s, a);

@@ -117,8 +117,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 // Rotation of pairs (v0, v1) and (v2, v3) by the angles whose (cos, sin) are
-// (cs[0], cs[1]) and (cs[2], cs[3]) (the 2x2 rotation display of the Rotary
-// positional encoding page: first member c*z0 - s*z1, second s*z0 + c*z1).
+// (cs[0], cs[1]) and (cs[2], cs[3]) (Grouped-query attention page, "All 13
+// steps", the 2x2 rotation display: first member c*z0 - s*z1, second
+// s*z0 + c*z1).
 __device__ __forceinline__ void rotate_pairs(float& v0, float& v1, float& v2, float& v3, f32x4 cs) {
   const float r0 = v0 * cs[0] - v1 * cs[1];
   const float r1 = v0 * cs[1] + v1 * cs[0];
@@ -185,16 +186,8 @@ struct GemmCfg {
   // (128x256: W_O at M = 2048 fetches 134 instead of 168 MB), 4 otherwise
   // (256x192: QKV fetches 172 instead of 192 MB; 256x256 at M = 32768 1-2 %
   // faster than with 8).
-#ifdef GQA_GEMM_GROUP
-  static constexpr int GROUP = GQA_GEMM_GROUP;   // build-time override (tuning sweeps)
-#else
   static constexpr int GROUP = 2 * FEAT >= 3 * TOK ? 8 : 4;
-#endif
-#ifdef GQA_GEMM_RPM
-  static constexpr int RPM = GQA_GEMM_RPM;   // build-time override (tuning sweeps)
-#else
   static constexpr int RPM = NP * NQ / (NP + NQ) > 1 ? NP * NQ / (NP + NQ) : 1;   // MFMAs per spread read
-#endif
   // Tiles of 64 tokens serve M <= 64 (decode), a single token tile: every weight
   // row is read by exactly one workgroup, once, so those loads stream past the
   // caches (non-temporal). Load instruction j of every wave fills P rows iff
@@ -552,7 +545,6 @@ static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
   return hipGetLastError();
 }
 
-#ifndef GQA_GEMM_NO_LAUNCHERS
 constexpr int SPLITK_MAX_M = 64;
 constexpr int SPLITK = 4;
 constexpr int GEMM_CUS = 256;   // CUs a launch is sized for (MI355X)
@@ -654,6 +646,5 @@ hipError_t launch_mlp_down(const uint16_t* act, const uint16_t* w2, int M, float
   if (M > SPLITK_MAX_M && M <= 4096) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
   return launch_fp32_out(a, splitk, s);
 }
-#endif
 
 }  // namespace gqa
