@@ -39,3 +39,21 @@ def test_decode_bytes_by_hand():
     weights = 2 * (4096 * 4096 * 2 + 1024 * 4096 * 2)
     kv = B * (S - 1) * 8 * 128 * 2 * 2
     assert bench.decode_bytes(B, S) == weights + kv + B * 1024 * 4 + B * 4096 * 6 + 512 == 2232943104
+
+
+def test_sampled_rows_flops_by_hand():
+    # K and V of every position; Q and the W_O product of each sampled row;
+    # row t attends to t + 1 keys
+    T, rows = 1000, [0, 5, 999]
+    kv = 2 * T * (1024 * 4096 * 2)
+    qo = 2 * 3 * (4096 * 4096 * 2)
+    att = 4 * 32 * 128 * (1 + 6 + 1000)
+    assert bench.rows_flops(T, rows) == kv + qo + att
+
+
+def test_headline_is_the_largest_workload():
+    # the line quotes the largest single-GPU prefill workload; every other
+    # workload has its own entry
+    sizes = {n: w[1] * w[2] for n, w in bench.WORKLOADS.items() if w[0] == "prefill"}
+    assert bench.HEADLINE == max(sizes, key=sizes.get)
+    assert {w[0] for w in bench.WORKLOADS.values()} == {"prefill", "decode"}
