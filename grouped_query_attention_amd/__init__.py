@@ -61,6 +61,7 @@ def _load():
         "gqa_chunk_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_block_forward": (I, [P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_decode_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P, Z, P]),
+        "gqa_decode_forward_static": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P]),
         "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, P]),
         "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P, Z, P]),
         "gqa_output_projection": (I, [P, P, I, P, P]),
@@ -94,7 +95,7 @@ def exported_symbols():
             "gqa_prefill_workspace_bytes",
             "gqa_decode_workspace_bytes", "gqa_attention_workspace_bytes",
             "gqa_chunk_workspace_bytes", "gqa_block_forward", "gqa_chunk_forward",
-            "gqa_decode_forward",
+            "gqa_decode_forward", "gqa_decode_forward_static",
             "gqa_qkv_rope", "gqa_attention", "gqa_output_projection", "gqa_decode_attention",
             "gqa_block_forward_prenorm", "gqa_chunk_forward_prenorm",
             "gqa_decode_forward_prenorm", "gqa_rmsnorm", "gqa_mlp_workspace_bytes",
@@ -242,6 +243,32 @@ def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int
         _req(norm_w, torch.bfloat16, (D_MODEL,), "norm_w")
         _check("gqa_decode_forward_prenorm",
                _load().gqa_decode_forward_prenorm(_ptr(x), _ptr(norm_w), float(eps), *args))
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_forward_static(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,
+                          out=None, h_out=None, stream=None):
+    """decode_forward without a workspace: the library's fixed per-GPU device
+    array (STATIC_SCRATCH_BYTES) holds the step's scratch, so the call allocates
+    nothing when `out` is given. Calls that overlap in time on one GPU race."""
+    import torch
+    B = x.shape[0]
+    S_max = k_cache.shape[1]
+    _req(x, torch.bfloat16, (B, D_MODEL), "x")
+    _req(rope, torch.float32, (N_PAIRS, 2), "rope")
+    _req(k_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "k_cache")
+    _req(v_cache, torch.bfloat16, (B, S_max, N_KV_HEADS, D_HEAD), "v_cache")
+    if out is None:
+        out = torch.empty((B, D_MODEL), dtype=torch.float32, device=x.device)
+    _req(out, torch.float32, (B, D_MODEL), "out")
+    if h_out is not None:
+        _req(h_out, torch.bfloat16, (B, N_HEADS, D_HEAD), "h_out")
+    _check("gqa_decode_forward_static", _load().gqa_decode_forward_static(
+        _ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_o), _ptr(rope), _ptr(k_cache),
+        _ptr(v_cache), B, S_max, int(start_pos), _ptr(out), _ptr(h_out), _stream(stream)))
     return out
 
 

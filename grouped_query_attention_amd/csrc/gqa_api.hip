@@ -2,8 +2,10 @@
 // workspace carve-up, and the kernel sequence of each entry point.
 // Semantics, layouts and error codes are documented in include/gqa.h.
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "gqa.h"
 #include "gqa_device.h"
@@ -215,11 +217,11 @@ int chunk_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
   return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, norm ? x : nullptr, part, s));
 }
 
-int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
-                const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
-                const float* rope, gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
-                int start_pos, float* out, gqa_bf16* h_out, void* workspace,
-                size_t workspace_bytes, void* stream) {
+// Every argument check of a decode step except the workspace.
+int decode_check(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
+                 const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
+                 const float* rope, const gqa_bf16* k_cache, const gqa_bf16* v_cache, int B,
+                 int S_max, int start_pos, const float* out, const gqa_bf16* h_out) {
   if (!x || !rope || !k_cache || !v_cache || !out) return GQA_ERR_NULL;
   int st = check_weights(w_q, w_k, w_v, w_o);
   if (st == GQA_OK && norm) st = check_prenorm(*norm);
@@ -229,6 +231,17 @@ int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
   if (misaligned(x) || misaligned(rope) || misaligned(k_cache) || misaligned(v_cache) ||
       misaligned(out) || (h_out && misaligned(h_out)))
     return GQA_ERR_ALIGN;
+  return GQA_OK;
+}
+
+int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
+                const gqa_bf16* w_k, const gqa_bf16* w_v, const gqa_bf16* w_o,
+                const float* rope, gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
+                int start_pos, float* out, gqa_bf16* h_out, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  const int st = decode_check(x, norm, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max,
+                              start_pos, out, h_out);
+  if (st != GQA_OK) return st;
   const DecodeWs L = decode_layout(B, S_max);
   if (!workspace || workspace_bytes < L.total) return GQA_ERR_WORKSPACE;
   if (misaligned(workspace)) return GQA_ERR_ALIGN;
@@ -281,6 +294,41 @@ int mlp_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w1, const g
   return hip_status(gqa::launch_mlp_down(act, w2, M, out, norm ? x : nullptr, part, s));
 }
 
+// Device scratch of gqa_decode_forward_static: one array per GPU the library
+// runs on, held until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[GQA_STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<void*> scratch_ptr[MAX_DEVICES];
+std::mutex scratch_init;
+
+// Device address of `scratch` on the current device, looked up on the first
+// call for that device; null (with *err set) if the lookup fails.
+void* scratch_address(hipError_t* err) {
+  *err = hipSuccess;
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= MAX_DEVICES) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(scratch_init);
+  p = scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if ((*err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess || !p) {
+      if (*err == hipSuccess) *err = hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,6 +343,9 @@ const char* gqa_status_string(int s) {
     case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED: request not implemented";
     case GQA_ERR_HIP: return "GQA_ERR_HIP: a HIP launch failed";
     case GQA_ERR_ARG: return "GQA_ERR_ARG: inconsistent arguments";
+    case GQA_ERR_TOO_LARGE:
+      return "GQA_ERR_TOO_LARGE: the request needs more scratch than the fixed device array of "
+             "the no-allocation entry holds";
     default: return "GQA_ERR_UNKNOWN";
   }
 }
@@ -460,6 +511,23 @@ int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w
                        void* stream) {
   return decode_impl(x, nullptr, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max,
                      start_pos, out, h_out, workspace, workspace_bytes, stream);
+}
+
+int gqa_decode_forward_static(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                              const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                              gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
+                              int start_pos, float* out, gqa_bf16* h_out, void* stream) {
+  // every argument is checked before the first HIP call (the scratch lookup)
+  const int st = decode_check(x, nullptr, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max,
+                              start_pos, out, h_out);
+  if (st != GQA_OK) return st;
+  const size_t need = decode_layout(B, S_max).total;
+  if (need > (size_t)GQA_STATIC_SCRATCH_BYTES) return GQA_ERR_TOO_LARGE;
+  hipError_t e;
+  void* ws = scratch_address(&e);
+  if (!ws) return GQA_ERR_HIP;
+  return decode_impl(x, nullptr, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, B, S_max,
+                     start_pos, out, h_out, ws, (size_t)GQA_STATIC_SCRATCH_BYTES, stream);
 }
 
 int gqa_decode_forward_prenorm(const gqa_bf16* x, const gqa_bf16* norm_w, float eps,

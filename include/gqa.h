@@ -25,9 +25,10 @@
  *    before any HIP call; a rejected call launches nothing and writes
  *    nothing. GQA_ERR_HIP reports a failed launch. Faults inside a kernel
  *    surface at the caller's next synchronisation, not here.
- *  - Calls on one stream are ordered; the library keeps no mutable state, so
- *    calls on different streams with disjoint outputs and workspaces may run
- *    concurrently.
+ *  - Calls on one stream are ordered; apart from gqa_decode_forward_static
+ *    (which holds one fixed device array per GPU, see there) the library
+ *    keeps no mutable state, so calls on different streams with disjoint
+ *    outputs and workspaces may run concurrently.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -49,7 +50,8 @@ typedef enum {
   GQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
   GQA_ERR_UNSUPPORTED = 5, /* a valid request this build does not implement      */
   GQA_ERR_HIP = 6,         /* a HIP launch failed                                 */
-  GQA_ERR_ARG = 7          /* inconsistent flags (e.g. causal with a mask)       */
+  GQA_ERR_ARG = 7,         /* inconsistent flags (e.g. causal with a mask)       */
+  GQA_ERR_TOO_LARGE = 8    /* more scratch than gqa_decode_forward_static holds   */
 } gqa_status;
 
 #define GQA_D_MODEL 4096
@@ -58,6 +60,7 @@ typedef enum {
 #define GQA_D_HEAD 128
 #define GQA_N_PAIRS 64
 #define GQA_MAX_TOKENS (1 << 24) /* B*T limit of one call */
+#define GQA_STATIC_SCRATCH_BYTES (16u << 20) /* device array of gqa_decode_forward_static */
 
 /* Human-readable name of a status code. Never NULL. */
 const char* gqa_status_string(int status);
@@ -182,6 +185,31 @@ int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w
                        gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
                        int start_pos, float* out, gqa_bf16* h_out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/*
+ * gqa_decode_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Same arguments, kernels and results as
+ * gqa_decode_forward, minus workspace / workspace_bytes: the scratch those
+ * kernels need (Q_r, H and the split partials) lives in a fixed device array
+ * of GQA_STATIC_SCRATCH_BYTES (16 MiB) that the library holds on each GPU it
+ * runs on until the process ends. The call allocates and frees nothing.
+ *  - Accepted when gqa_decode_workspace_bytes(B, S_max) <= 16 MiB, which holds
+ *    for every B <= 256 at any S_max; larger requests return
+ *    GQA_ERR_TOO_LARGE and launch nothing.
+ *  - The first call on a device looks up the array's device address there
+ *    (hipGetSymbolAddress, not a stream operation; GQA_ERR_HIP if it fails).
+ *    This per-device address is the only state the library keeps.
+ *  - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *    time on the same GPU (different streams, or several host threads) race
+ *    and give undefined results. Calls on one stream are ordered and safe.
+ *    The array keeps the last call's contents; nothing in it needs to start
+ *    at zero.
+ */
+int gqa_decode_forward_static(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
+                              const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
+                              gqa_bf16* k_cache, gqa_bf16* v_cache, int B, int S_max,
+                              int start_pos, float* out, gqa_bf16* h_out, void* stream);
 
 /*
  * The attention half of the decoder block with its handoff ("Llama 3.1 8B ·

@@ -19,7 +19,7 @@ from oracle import gqa_oracle as O
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gqa.h")
 
-OK, NULL, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, HIP, ARG = range(8)
+OK, NULL, SHAPE, ALIGN, WORKSPACE, UNSUPPORTED, HIP, ARG, TOO_LARGE = range(9)
 FAKE = 0x10000          # aligned, never dereferenced
 MIS = 0x10004           # not 16-byte aligned
 
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_dims():
     lib = gqa.lib()
-    for s in range(8):
+    for s in range(9):
         assert lib.gqa_status_string(s).decode().startswith("GQA_")
     assert lib.gqa_status_string(99).decode() == "GQA_ERR_UNKNOWN"
     assert gqa.dims() == (4096, 32, 8, 128)
@@ -152,6 +152,38 @@ def _dec(**kw):
 ])
 def test_decode_forward_rejects(kw, want):
     assert _dec(**kw) == want
+
+
+def _dec_static(**kw):
+    a = dict(x=FAKE, wq=FAKE, wk=FAKE, wv=FAKE, wo=FAKE, rope=FAKE, kc=FAKE, vc=FAKE, B=64,
+             S=8192, sp=8191, out=FAKE, h=None, stream=None)
+    a.update(kw)
+    return gqa.lib().gqa_decode_forward_static(a["x"], a["wq"], a["wk"], a["wv"], a["wo"],
+                                               a["rope"], a["kc"], a["vc"], a["B"], a["S"],
+                                               a["sp"], a["out"], a["h"], a["stream"])
+
+
+# every check runs before the first HIP call (the scratch lookup), so these
+# return without touching a GPU; B = 1024 needs more than the 16 MiB array
+@pytest.mark.parametrize("kw,want", [
+    (dict(kc=None), NULL), (dict(x=None), NULL), (dict(wo=None), NULL), (dict(rope=None), NULL),
+    (dict(sp=8192), SHAPE), (dict(sp=-1), SHAPE), (dict(B=0), SHAPE), (dict(S=0), SHAPE),
+    (dict(vc=MIS), ALIGN), (dict(out=MIS), ALIGN), (dict(h=MIS), ALIGN),
+    (dict(B=1024), TOO_LARGE), (dict(B=1 << 16, S=4, sp=3), TOO_LARGE),
+])
+def test_decode_forward_static_rejects(kw, want):
+    assert _dec_static(**kw) == want
+
+
+def test_static_scratch_holds_every_batch_up_to_256():
+    # the no-allocation decode entry accepts exactly the requests whose
+    # workspace fits its fixed array; the header promises every B <= 256 at any
+    # cache length (the split-KV partials are bounded by the 512-item plan)
+    assert gqa.STATIC_SCRATCH_BYTES == 16 << 20
+    for B in range(1, 257):
+        for S in (1, 17, 4096, 8192, 65536, 1 << 20):
+            assert gqa.decode_workspace_bytes(B, S) <= gqa.STATIC_SCRATCH_BYTES, (B, S)
+    assert gqa.decode_workspace_bytes(1024, 8192) > gqa.STATIC_SCRATCH_BYTES
 
 
 def _chk(**kw):
