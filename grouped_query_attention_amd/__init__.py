@@ -246,7 +246,7 @@ def decode_forward(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int
     return out
 
 
-STATIC_SCRATCH_BYTES = 16 << 20
+STATIC_SCRATCH_BYTES = 32 << 20
 
 
 def decode_forward_static(x, w_q, w_k, w_v, w_o, rope, k_cache, v_cache, start_pos: int, *,

@@ -545,12 +545,23 @@ static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Split reduction for few tokens (with a workspace): M <= 64 takes one 64-token
+// tile and 4 slices of K (weight streams, non-temporal); 64 < M <= 256 takes
+// 128-token tiles and 8 slices up to M = 128, 4 above, so that a launch still
+// has 256-768 workgroups (unsplit 128x128 tiles give 48 workgroups for the QKV
+// product at M = 128) while the partials stay within 1024 rows of 6144 floats.
 constexpr int SPLITK_MAX_M = 64;
 constexpr int SPLITK = 4;
+constexpr int SPLITK_MID_M = 256;
 constexpr int GEMM_CUS = 256;   // CUs a launch is sized for (MI355X)
 
+// K slices of the split reduction for M tokens (0: not split)
+inline int splitk_slices(int M) {
+  return M <= SPLITK_MAX_M ? SPLITK : M <= 128 ? 8 : M <= SPLITK_MID_M ? 4 : 0;
+}
+
 size_t gemm_splitk_bytes(int M) {
-  return M <= SPLITK_MAX_M ? (size_t)SPLITK * M * N_QKV * sizeof(float) : 0;
+  return (size_t)splitk_slices(M) * M * N_QKV * sizeof(float);
 }
 
 // Products with 4096 fp32 output features (W_O, the MLP's down product), by M:
@@ -561,6 +572,8 @@ size_t gemm_splitk_bytes(int M) {
 static hipError_t launch_fp32_out(GemmArgs a, float* splitk, hipStream_t s) {
   const int M = a.M;
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
+  if (M <= 128 && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 8>(a, splitk, s);
+  if (M <= SPLITK_MID_M && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 4>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
   if (M < 4096) return launch_gemm<128, 256, 2, 4, 2, EPI_OUT_F32>(a, s);
@@ -580,6 +593,8 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
   // Few tokens (decode): split K with a workspace, else thin weight strips and a
   // deep load ring; otherwise the largest tile that still fills the chip.
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4, SPLITK>(a, splitk, s);
+  if (M <= 128 && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 8>(a, splitk, s);
+  if (M <= SPLITK_MID_M && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 4>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);
   // 192-wide feature tiles: 256 tokens x 192 features give exactly one

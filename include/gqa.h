@@ -60,7 +60,7 @@ typedef enum {
 #define GQA_D_HEAD 128
 #define GQA_N_PAIRS 64
 #define GQA_MAX_TOKENS (1 << 24) /* B*T limit of one call */
-#define GQA_STATIC_SCRATCH_BYTES (16u << 20) /* device array of gqa_decode_forward_static */
+#define GQA_STATIC_SCRATCH_BYTES (32u << 20) /* device array of gqa_decode_forward_static */
 
 /* Human-readable name of a status code. Never NULL. */
 const char* gqa_status_string(int status);
@@ -192,9 +192,9 @@ int gqa_decode_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w
  * harnesses that forbid allocation). Same arguments, kernels and results as
  * gqa_decode_forward, minus workspace / workspace_bytes: the scratch those
  * kernels need (Q_r, H and the split partials) lives in a fixed device array
- * of GQA_STATIC_SCRATCH_BYTES (16 MiB) that the library holds on each GPU it
+ * of GQA_STATIC_SCRATCH_BYTES (32 MiB) that the library holds on each GPU it
  * runs on until the process ends. The call allocates and frees nothing.
- *  - Accepted when gqa_decode_workspace_bytes(B, S_max) <= 16 MiB, which holds
+ *  - Accepted when gqa_decode_workspace_bytes(B, S_max) <= 32 MiB, which holds
  *    for every B <= 256 at any S_max; larger requests return
  *    GQA_ERR_TOO_LARGE and launch nothing.
  *  - The first call on a device looks up the array's device address there
