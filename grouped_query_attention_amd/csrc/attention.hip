@@ -36,7 +36,7 @@ namespace gqa {
 
 constexpr float LOG2E = 1.4426950408889634f;
 // log2(e) / sqrt(128): one multiply turns a raw score into the base-2 exponent.
-constexpr float SCALE_LOG2 = 0.12751743082459868f;
+constexpr float SCALE_LOG2 = QK_SCALE_LOG2;
 constexpr float SQRT_DH = 11.313708498984761f;
 constexpr float NEG_INF = -__builtin_inff();
 
@@ -53,7 +53,8 @@ constexpr int FA_NI_W = 4;       // 1-KiB direct-to-LDS loads per wave per tile 
 // Lazy rescaling: the reference max of a row only moves when a score exceeds it
 // by 8 in base 2 (probabilities then stay <= 2^8), so the O rescale is skipped
 // for almost every tile. Expressed in raw-score units.
-constexpr float FA_RESCALE_RAW = 8.0f / SCALE_LOG2;
+constexpr float FA_RESCALE_LOG2 = 8.0f;
+constexpr float FA_RESCALE_RAW = FA_RESCALE_LOG2 / SCALE_LOG2;
 
 // K tile [64 keys][128 d], 256-byte rows: 16-byte chunk c of key k at chunk
 // c ^ (k & 15), so the 16 lanes of a fragment read (16 keys, one chunk) hit 16
@@ -96,7 +97,8 @@ constexpr int FA_MIN_PIECE = 4;    // key tiles: bins never hold fewer
 constexpr int FA_ENTRY_COST = 4;   // key-tile trips an entry costs beyond its tiles (plan balance)
 constexpr int FA_DIRECT = 255;     // slot value of an entry that writes H itself
 // Partial of one piece for one (sequence, KV head): O[4 heads][64 rows][128],
-// then max[4][64], then sum[4][64], fp32.
+// then max[4][64] (base-2 units: the score times log2(e)/sqrt(128)), then
+// sum[4][64], fp32.
 constexpr int FA_PART = N_REP * FA_BQ * D_HEAD + 2 * N_REP * FA_BQ;
 constexpr int FA_MERGE_ROWS = 8;   // (head, query) rows per merge workgroup
 
@@ -107,6 +109,8 @@ struct FlashArgs {
   uint16_t* h;
   float* part;           // piece partials [slot][B][8][FA_PART] (planned launches)
   int B, T, kv_len, q_pos0, causal, n_qtiles;
+  // the queries carry the factor log2(e)/sqrt(128) already (QKV epilogue of the
+  // block paths), so a score MFMA yields the base-2 exponent directly
   // planned launch: workgroup i runs bin i / (8B) for (b, g) = split of i % (8B),
   // i.e. entries bin_start[bin] .. bin_start[bin + 1] - 1, each
   // qtile | first key tile << 8 | end key tile << 16 | slot << 24
@@ -122,6 +126,10 @@ struct FlashMergeArgs {
 };
 
 // One (query tile, key tiles kt0..kt1-1) entry for (sequence b, KV head g).
+// QS: the queries are pre-scaled by log2(e)/sqrt(128) (see FlashArgs); the
+// score MFMA chain then starts from minus the row's reference, so each
+// accumulator is the exponent of its probability with no VALU work.
+template <bool QS>
 __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, int b, int g,
                                             int qt, int kt0, int kt1, int slot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -184,9 +192,13 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   f32x16 o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-  float m_ref = NEG_INF;   // reference max of this lane's query row, raw-score units
+  float m_ref = NEG_INF;   // reference max of this lane's query row (raw-score units; base 2 if QS)
   float l_run = 0.f;       // this lane's share of the row sum (relative to m_ref)
   u32x4 pf[4];             // bf16 probabilities of the last softmax (P^T fragments)
+  // QS: the score chain starts from -m_eff, m_eff = m_ref or 0 while the row has
+  // no reference yet; thr is the rescale threshold on scores relative to m_eff
+  float m_eff = 0.f, thr = NEG_INF;
+  f32x16 negm = f32x16{};
 
   const bool has_mask = a.mask != nullptr;
   const float* mrow = has_mask ? a.mask + (size_t)(qi < a.T ? qi : 0) * a.kv_len : nullptr;
@@ -199,7 +211,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
     // three register buffers; the scheduling fences keep the compiler from
     // sinking the reads next to their use).
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = f32x16{};
+    for (int kb2 = 0; kb2 < 2; ++kb2) s[kb2] = QS ? negm : f32x16{};
     u32x4 kf[3][2];
     auto read_k = [&](int st, u32x4 (&f)[2]) {
 #pragma unroll
@@ -235,7 +247,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         for (int i = 0; i < 16; ++i) {
           const int kg = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
           float x = s[kb2][i];
-          if (has_mask && kg < a.kv_len && qi < a.T) x += mrow[kg] * SQRT_DH;
+          if (has_mask && kg < a.kv_len && qi < a.T) x += mrow[kg] * (QS ? LOG2E : SQRT_DH);
           if (kg >= a.kv_len || (a.causal && kg > qpos)) x = NEG_INF;
           s[kb2][i] = x;
         }
@@ -248,22 +260,53 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
     for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb2][i]);
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + FA_RESCALE_RAW) != 0) {
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const bool need = mx > m_ref + FA_RESCALE_RAW;   // false when mx = -inf
-      const float m_new = need ? mx : m_ref;
-      // lanes that keep their reference keep their sums (alpha 1: with m_ref = -inf,
-      // a row that has seen no key yet, the difference would be -inf - -inf = NaN);
-      // a first finite max gives alpha = 0 from m_ref = -inf
-      const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2) : 1.f;
-      m_ref = m_new;
-      l_run *= alpha;
+    float moff;
+    if constexpr (QS) {
+      // scores are relative to m_eff, in base-2 units
+      if (__builtin_amdgcn_ballot_w64(mx > thr) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need = mx > thr;                     // false when mx = -inf
+        const float m_new = need ? mx + m_eff : m_ref;
+        // as below: a row that keeps its reference keeps its sums; a first finite
+        // maximum gives alpha = 0 from m_ref = -inf
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.f;
+        m_ref = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+        // this tile's scores move to the new reference, and so does the next chain
+        const float m_eff_new = m_ref == NEG_INF ? 0.f : m_ref;
+        const float shift = m_eff - m_eff_new;
+        m_eff = m_eff_new;
+        thr = m_ref == NEG_INF ? NEG_INF : FA_RESCALE_LOG2;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negm[i] = -m_eff;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s[kb2][i] += shift;
+      }
+      moff = 0.f;
+    } else {
+      if (__builtin_amdgcn_ballot_w64(mx > m_ref + FA_RESCALE_RAW) != 0) {
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool need = mx > m_ref + FA_RESCALE_RAW;   // false when mx = -inf
+        const float m_new = need ? mx : m_ref;
+        // lanes that keep their reference keep their sums (alpha 1: with m_ref = -inf,
+        // a row that has seen no key yet, the difference would be -inf - -inf = NaN);
+        // a first finite max gives alpha = 0 from m_ref = -inf
+        const float alpha = need ? __builtin_amdgcn_exp2f((m_ref - m_new) * SCALE_LOG2) : 1.f;
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[db][i] *= alpha;
+      }
+      moff = (m_ref == NEG_INF) ? 0.f : -m_ref * SCALE_LOG2;
     }
-    const float moff = (m_ref == NEG_INF) ? 0.f : -m_ref * SCALE_LOG2;
     // The row sum adds the bf16 probabilities the P·V MFMA uses, two per dot2
     // instruction against (1, 1): half the VALU work of fp32 adds, and the
     // numerator and denominator then weight the same rounded values.
@@ -276,9 +319,11 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         bf16x2 pb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const f32x2 pp = {
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e], SCALE_LOG2, moff)),
-              __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e + 1], SCALE_LOG2, moff))};
+          const f32x2 pp =
+              QS ? f32x2{__builtin_amdgcn_exp2f(s[kb2][8 * hf + 2 * e]),
+                         __builtin_amdgcn_exp2f(s[kb2][8 * hf + 2 * e + 1])}
+                 : f32x2{__builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e], SCALE_LOG2, moff)),
+                         __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][8 * hf + 2 * e + 1], SCALE_LOG2, moff))};
           pb[e] = __builtin_convertvector(pp, bf16x2);
         }
         ls0 = __builtin_amdgcn_fdot2_f32_bf16(pb[0], ones, ls0, false);
@@ -360,7 +405,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         *reinterpret_cast<f32x4*>(orow + db * 32 + gq * 8) =
             f32x4{o[db][4 * gq], o[db][4 * gq + 1], o[db][4 * gq + 2], o[db][4 * gq + 3]};
     if (lhalf == 0) {
-      pp[N_REP * FA_BQ * D_HEAD + row] = m_ref;
+      pp[N_REP * FA_BQ * D_HEAD + row] = QS ? m_ref : m_ref * SCALE_LOG2;   // base 2
       pp[N_REP * FA_BQ * D_HEAD + N_REP * FA_BQ + row] = l_tot;
     }
     return;
@@ -379,6 +424,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   }
 }
 
+template <bool QS>
 __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[FA_STAGES * 2 * FA_TILE];
   const int g = blockIdx.x & (N_KV - 1);
@@ -391,7 +437,7 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
       const unsigned e = a.ent[i];
       // every wave is done with the LDS ring of the previous entry
       if (i > a.bin_start[bin]) barrier_no_fence();
-      flash_entry(a, smem, b, g, e & 255, (e >> 8) & 255, (e >> 16) & 255, e >> 24);
+      flash_entry<QS>(a, smem, b, g, e & 255, (e >> 8) & 255, (e >> 16) & 255, e >> 24);
     }
     return;
   }
@@ -399,13 +445,14 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   const int qt = a.causal ? (a.n_qtiles - 1 - rest / a.B) : (rest / a.B);
   int kv_end = a.kv_len;
   if (a.causal) kv_end = min(kv_end, a.q_pos0 + (qt + 1) * FA_BQ);
-  flash_entry(a, smem, b, g, qt, 0, (kv_end + FA_BN - 1) / FA_BN, FA_DIRECT);
+  flash_entry<QS>(a, smem, b, g, qt, 0, (kv_end + FA_BN - 1) / FA_BN, FA_DIRECT);
 }
 
 // Combines the pieces of cut query tiles. Workgroup (r, t, b, g) takes rows
 // 8r .. 8r+7 of (head, query) of cut tile t; each 32-lane half-wave takes one
 // row, lane i holding d = 4i .. 4i+3. Pieces are rescaled to their common max
-// and summed, then divided by the summed row sums (pieces in slot order).
+// and summed, then divided by the summed row sums (pieces in slot order). The
+// pieces' maxima are in base-2 units.
 __global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
   constexpr int MAXP = 4;
   const int g = blockIdx.x & (N_KV - 1);
@@ -441,7 +488,7 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
   float L = 0.f;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
-    const float f = mp[p] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f((mp[p] - M) * SCALE_LOG2);
+    const float f = mp[p] == NEG_INF ? 0.f : __builtin_amdgcn_exp2f(mp[p] - M);
     acc += op[p] * f;
     L += lp[p] * f;
   }
@@ -579,7 +626,7 @@ size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal) {
 hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
                                   long long kv_bstride, const float* mask, int causal, int B,
                                   int T, int kv_len, int q_pos0, uint16_t* h_out,
-                                  float* partials, hipStream_t s) {
+                                  float* partials, bool q_scaled, hipStream_t s) {
   FlashArgs a{};
   a.q = q_r; a.k = k; a.v = v; a.kv_bstride = kv_bstride; a.mask = mask; a.h = h_out;
   a.B = B; a.T = T; a.kv_len = kv_len; a.q_pos0 = q_pos0; a.causal = causal;
@@ -594,7 +641,10 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
     for (int i = 0; i < plan.n_ent; ++i) a.ent[i] = plan.ent[i];
     grid = (long long)plan.n_bins * B * N_KV;
   }
-  hipLaunchKernelGGL(flash_fwd_kernel, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  if (q_scaled)
+    hipLaunchKernelGGL(flash_fwd_kernel<true>, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL(flash_fwd_kernel<false>, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !planned || plan.n_merge == 0) return e;
   FlashMergeArgs m{};

@@ -62,6 +62,7 @@ struct GemmArgs {
   // rotation epilogue
   const float* rope;     // [T][64][2]
   int T;                 // tokens per sequence (rope row = token % T)
+  float q_scale;         // factor on the rotated Q features before rounding (1: none)
   uint16_t* q_dst; long long q_bstride, q_rstride;     // elements
   uint16_t* k_dst; uint16_t* v_dst; long long kv_bstride, kv_rstride;
   // fp32 epilogue: out[M][N]; split-K partials: out + blockIdx.y*M*N
@@ -374,6 +375,9 @@ void gemm_nt_kernel(GemmArgs a) {
         float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
         if (rot)
           rotate_pairs(v0, v1, v2, v3, *reinterpret_cast<const f32x4*>(rrow + (f & (D_HEAD - 1))));
+        if (fblk < D_MODEL) {
+          v0 *= a.q_scale; v1 *= a.q_scale; v2 *= a.q_scale; v3 *= a.q_scale;
+        }
         const int c = (wp * C::WP + i * 16 + 4 * lg) >> 3;
         *reinterpret_cast<u32x2*>(tile + tl * FEAT + ((c ^ (tl & SWZ)) << 3) + 4 * (lg & 1)) =
             u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
@@ -496,6 +500,9 @@ __global__ __launch_bounds__(256) void splitk_qkv_rope_kernel(GemmArgs a) {
   if (col < D_MODEL + N_KV * D_HEAD)
     rotate_pairs(v0, v1, v2, v3,
                  *reinterpret_cast<const f32x4*>(a.rope + (size_t)t * (2 * 64) + (col & (D_HEAD - 1))));
+  if (col < D_MODEL) {
+    v0 *= a.q_scale; v1 *= a.q_scale; v2 *= a.q_scale; v3 *= a.q_scale;
+  }
   u32x2 w = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
   *reinterpret_cast<u32x2*>(dst) = w;
 }
@@ -584,10 +591,10 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
-                           long long kv_rstride, float* splitk, hipStream_t s) {
+                           long long kv_rstride, float* splitk, float q_scale, hipStream_t s) {
   GemmArgs a{};
   a.act = x; a.w0 = wq; a.w1 = wk; a.w2 = wv; a.M = M; a.N = N_QKV; a.K = D_MODEL;
-  a.rope = rope; a.T = T;
+  a.rope = rope; a.T = T; a.q_scale = q_scale;
   a.q_dst = q_dst; a.q_bstride = q_bstride; a.q_rstride = q_rstride;
   a.k_dst = k_dst; a.v_dst = v_dst; a.kv_bstride = kv_bstride; a.kv_rstride = kv_rstride;
   // Few tokens (decode): split K with a workspace, else thin weight strips and a

@@ -164,12 +164,13 @@ int block_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
   const gqa_bf16* xin =
       norm_input(norm, x, (int)M, reinterpret_cast<gqa_bf16*>(ws + L.h), s, &e);
   if (e != hipSuccess) return GQA_ERR_HIP;
+  // Q_r is stored pre-scaled by log2(e)/sqrt(128) for the attention (internal)
   e = gqa::launch_qkv_rope(xin, w_q, w_k, w_v, rope, (int)M, T, q,
                            (long long)T * D_MODEL, D_MODEL, k, v,
-                           (long long)T * KV_W, KV_W, part, s);
+                           (long long)T * KV_W, KV_W, part, gqa::QK_SCALE_LOG2, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_flash_attention(q, k, v, (long long)T * KV_W, mask, causal, B, T, kv_len, 0,
-                                  h, part, s);
+                                  h, part, true, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, norm ? x : nullptr, part, s));
 }
@@ -209,10 +210,10 @@ int chunk_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
                            (long long)T * D_MODEL, D_MODEL,
                            k_cache + (size_t)start_pos * KV_W,
                            v_cache + (size_t)start_pos * KV_W, cache_bstride, KV_W,
-                           part, s);
+                           part, gqa::QK_SCALE_LOG2, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_flash_attention(q, k_cache, v_cache, cache_bstride, nullptr, 1, B, T,
-                                  start_pos + T, start_pos, h, part, s);
+                                  start_pos + T, start_pos, h, part, true, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   return hip_status(gqa::launch_out_proj(h, w_o, (int)M, out, norm ? x : nullptr, part, s));
 }
@@ -259,7 +260,7 @@ int decode_impl(const gqa_bf16* x, const PreNorm* norm, const gqa_bf16* w_q,
   e = gqa::launch_qkv_rope(xin, w_q, w_k, w_v, rope, B, 1, q, D_MODEL, 0,
                            k_cache + (size_t)start_pos * KV_W,
                            v_cache + (size_t)start_pos * KV_W, cache_bstride, 0,
-                           part, s);
+                           part, 1.0f, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
   e = gqa::launch_decode_attention(q, k_cache, v_cache, B, S_max, start_pos + 1, part, h, s);
   if (e != hipSuccess) return GQA_ERR_HIP;
@@ -416,7 +417,7 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
   const long long M = (long long)B * T;
   return hip_status(gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q_r,
                                          (long long)T * D_MODEL, D_MODEL, k_r, v,
-                                         (long long)T * KV_W, KV_W, nullptr,
+                                         (long long)T * KV_W, KV_W, nullptr, 1.0f,
                                          (hipStream_t)stream));
 }
 
@@ -435,7 +436,7 @@ int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
   if (workspace && workspace_bytes < need) return GQA_ERR_WORKSPACE;
   float* part = workspace && need ? static_cast<float*>(workspace) : nullptr;
   return hip_status(gqa::launch_flash_attention(q_r, k_r, v, (long long)kv_len * KV_W, mask,
-                                                causal, B, T, kv_len, 0, h_out, part,
+                                                causal, B, T, kv_len, 0, h_out, part, false,
                                                 (hipStream_t)stream));
 }
 

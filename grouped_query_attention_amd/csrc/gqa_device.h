@@ -13,6 +13,8 @@ constexpr int D_HEAD = 128;
 constexpr int N_REP = N_HEADS / N_KV;     // query heads per KV head (4)
 constexpr int N_QKV = D_MODEL + 2 * N_KV * D_HEAD;  // 6144 fused projection columns
 constexpr int D_FF = 14336;               // SwiGLU MLP hidden width
+// log2(e)/sqrt(128): the score scale 1/sqrt(d_head) of the softmax, in base 2
+constexpr float QK_SCALE_LOG2 = 0.12751743082459868f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));

@@ -12,12 +12,14 @@ namespace gqa {
 //   Q row: q_dst + b*q_bstride + t*q_rstride           (4096 elements)
 //   K/V row: k_dst/v_dst + b*kv_bstride + t*kv_rstride  (1024 elements)
 // `splitk` (may be null) is fp32 scratch of gemm_splitk_bytes(M) bytes: with
-// it, M <= 64 products split the reduction across workgroups (decode).
+// it, M <= 256 products split the reduction across workgroups. The rotated Q
+// features are multiplied by q_scale before their rounding (1: plain Q_r;
+// QK_SCALE_LOG2: the form launch_flash_attention takes with q_scaled).
 hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t* wk,
                            const uint16_t* wv, const float* rope, int M, int T,
                            uint16_t* q_dst, long long q_bstride, long long q_rstride,
                            uint16_t* k_dst, uint16_t* v_dst, long long kv_bstride,
-                           long long kv_rstride, float* splitk, hipStream_t s);
+                           long long kv_rstride, float* splitk, float q_scale, hipStream_t s);
 
 // out[M][4096] (fp32) = h[M][4096] · w_oᵀ (+ resid[M][4096] bf16 when not null);
 // `splitk` as for launch_qkv_rope.
@@ -45,12 +47,13 @@ size_t gemm_splitk_bytes(int M);
 // sequence b start at k + b*kv_bstride (row stride 1024 elements); query i is
 // at position q_pos0 + i; keys 0..kv_len-1. `partials` (may be null: plain
 // launch) is fp32 scratch of flash_partials_bytes(B, T, kv_len, q_pos0, causal) bytes
-// for the balanced causal launch of few query tiles.
+// for the balanced causal launch of few query tiles. q_scaled: the queries
+// carry the factor QK_SCALE_LOG2 already (launch_qkv_rope's q_scale).
 size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal);
 hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
                                   long long kv_bstride, const float* mask, int causal, int B,
                                   int T, int kv_len, int q_pos0, uint16_t* h_out,
-                                  float* partials, hipStream_t s);
+                                  float* partials, bool q_scaled, hipStream_t s);
 
 // Split-KV decode attention: q_r [B][32][128]; caches [B][S_max][8][128];
 // keys 0..kv_len-1; h_out [B][32][128]. `partials` needs decode_partials_bytes.
