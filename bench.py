@@ -45,13 +45,13 @@ PARAMS_PER_BLOCK = 41_943_040  # W_Q + W_K + W_V + W_O
 # instantiation named here only: re-measure when it changes.
 PROFILED_TRAFFIC = {
     ("prefill_B1_T2048", "qkv_rope"): {"kernel": "gemm_nt_kernel<256, 192, 2, 4, 2, 0, 64>",
-                                       "bytes": 197.3e6},
-    ("prefill_B1_T2048", "attention"): {"kernel": "flash_fwd_kernel + flash_merge_kernel",
+                                       "bytes": 197.4e6},
+    ("prefill_B1_T2048", "attention"): {"kernel": "flash_fwd_kernel<true> + flash_merge_kernel",
                                         "bytes": 102.2e6},
     ("prefill_B1_T2048", "out_proj"): {"kernel": "gemm_nt_kernel<128, 256, 2, 4, 2, 1, 64>",
                                        "bytes": 168.0e6},
-    ("prefill_B1_T131072", "attention"): {"kernel": "flash_fwd_kernel (plain causal launch)",
-                                          "bytes": 19.594e9},
+    ("prefill_B1_T131072", "attention"): {"kernel": "flash_fwd_kernel<true> (plain causal launch)",
+                                          "bytes": 19.596e9},
 }
 
 HEADLINE = "prefill_B1_T131072"
@@ -211,18 +211,22 @@ class Bench:
             rec["cold_cache"] = {"median_ms": self.time_cold(step, args.steps),
                                  "note": "median step with a 512 MiB read between steps"}
 
-        # each stage alone (the stage entries launch exactly the kernels of the step)
-        q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope)
+        # each stage alone: with pre-scaled queries (q_scaled) and, above 256
+        # tokens, the stage entries launch exactly the kernels of the step
+        q_r, k_r, v = gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_scaled=True)
         aws_n = gqa.attention_workspace_bytes(B, T, T, True)
         aws = torch.empty(max(aws_n, 1), dtype=torch.uint8, device=self.dev)
-        hbuf = gqa.attention(q_r, k_r, v, causal=True, workspace=aws if aws_n else None)
+        hbuf = gqa.attention(q_r, k_r, v, causal=True, workspace=aws if aws_n else None,
+                             q_scaled=True)
         stages = {
             "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
-                         lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v)),
-            "attention": ("flash_fwd_kernel + flash_merge_kernel (balanced causal launch)"
-                          if aws_n else "flash_fwd_kernel",
+                         lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v,
+                                              q_scaled=True)),
+            "attention": ("flash_fwd_kernel<true> + flash_merge_kernel (balanced causal launch)"
+                          if aws_n else "flash_fwd_kernel<true> (pre-scaled queries)",
                           lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf,
-                                                workspace=aws if aws_n else None)),
+                                                workspace=aws if aws_n else None,
+                                                q_scaled=True)),
             "out_proj": ("gemm_nt_kernel (W_O GEMM, fp32 epilogue)",
                          lambda: gqa.output_projection(hbuf, w[3], out=out.view(B * T, 4096))),
         }
@@ -401,6 +405,18 @@ class Bench:
         self.log(f"[bench] pre-norm prefill: {ms_pre:.4f} ms vs plain {ms_plain:.4f} ms; "
                  f"rmsnorm {ms_norm * 1e3:.1f} us")
         del x, w, out, ws, y
+        # the normalisation kernel alone at the token counts of the larger prefills
+        norm_ms = {}
+        for M in (32768, 131072):
+            xm = torch.randn((M, 4096), device=self.dev).to(torch.bfloat16)
+            ym = torch.empty_like(xm)
+            norm_ms[M], _ = self.time_steps(lambda: gqa.rmsnorm(xm, g, y=ym), args.steps,
+                                            args.warmup)
+            del xm, ym
+        extra["rmsnorm_kernel_by_tokens"] = {
+            str(M): {"ms": v, "GB/s": 2 * M * 4096 * 2 / (v * 1e-3) / 1e9}
+            for M, v in norm_ms.items()}
+        self.log(f"[bench] rmsnorm alone: {', '.join(f'M={M} {v:.4f} ms' for M, v in norm_ms.items())}")
 
         Bd, S, sp = 64, 8192, 8191
         self.log("[bench] pre-norm + residual: decode B=64 kv=8192")
@@ -477,8 +493,9 @@ class Bench:
         q = torch.randn((B, T, 32, 128), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
         k = torch.randn((B, T, 8, 128), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
         v = torch.randn((B, T, 8, 128), dtype=torch.float32, device=self.dev).to(torch.bfloat16)
-        h = gqa.attention(q, k, v, causal=True)
-        ms, med = self.time_steps(lambda: gqa.attention(q, k, v, causal=True, h_out=h),
+        h = gqa.attention(q, k, v, causal=True, q_scaled=True)
+        ms, med = self.time_steps(lambda: gqa.attention(q, k, v, causal=True, h_out=h,
+                                                        q_scaled=True),
                                   args.steps, min(args.warmup, 1))
         F = stage_flops(B, T)["attention"]
         return {"stage": "attention", "ms": ms, "median_ms": med,

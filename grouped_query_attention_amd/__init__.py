@@ -62,8 +62,8 @@ def _load():
         "gqa_block_forward": (I, [P, P, P, P, P, P, P, I, I, I, I, P, P, P, Z, P]),
         "gqa_decode_forward": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P, Z, P]),
         "gqa_decode_forward_static": (I, [P, P, P, P, P, P, P, P, I, I, I, P, P, P]),
-        "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, P]),
-        "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P, Z, P]),
+        "gqa_qkv_rope": (I, [P, P, P, P, P, I, I, P, P, P, I, P]),
+        "gqa_attention": (I, [P, P, P, P, I, I, I, I, P, P, Z, I, P]),
         "gqa_output_projection": (I, [P, P, I, P, P]),
         "gqa_decode_attention": (I, [P, P, P, I, I, I, P, P, Z, P]),
         "gqa_block_forward_prenorm": (I, [P, P, F, P, P, P, P, P, P, I, I, I, I, P, P, P, Z,
@@ -359,8 +359,13 @@ def mlp_forward(x, w1, w2, w3, *, norm_w=None, eps: float = NORM_EPS, out=None, 
     return out
 
 
-def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None):
-    """Q_r [B,T,32,128], K_r [B,T,8,128], V [B,T,8,128] (bf16) for x [B,T,4096]."""
+def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, q_scaled: bool = False,
+             stream=None):
+    """Q_r [B,T,32,128], K_r [B,T,8,128], V [B,T,8,128] (bf16) for x [B,T,4096].
+
+    q_scaled: Q_r comes out multiplied by log2(e)/sqrt(128), the form the block's
+    own attention stage takes (attention(..., q_scaled=True)).
+    """
     import torch
     B, T, _ = x.shape
     _req(x, torch.bfloat16, (B, T, D_MODEL), "x")
@@ -372,16 +377,19 @@ def qkv_rope(x, w_q, w_k, w_v, rope, *, q_r=None, k_r=None, v=None, stream=None)
     if v is None:
         v = torch.empty((B, T, N_KV_HEADS, D_HEAD), dtype=torch.bfloat16, device=dev)
     st = _load().gqa_qkv_rope(_ptr(x), _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(rope), B, T,
-                              _ptr(q_r), _ptr(k_r), _ptr(v), _stream(stream))
+                              _ptr(q_r), _ptr(k_r), _ptr(v), int(bool(q_scaled)),
+                              _stream(stream))
     _check("gqa_qkv_rope", st)
     return q_r, k_r, v
 
 
 def attention(q_r, k_r, v, *, causal: bool = True, mask=None, h_out=None, workspace=None,
-              balanced: bool = True, stream=None):
+              balanced: bool = True, q_scaled: bool = False, stream=None):
     """H [B,T,32,128] bf16 from rotated queries/keys and values. With `balanced`
     (default) a causal launch of few query tiles gets its workspace (allocated
-    here unless given); balanced=False runs the plain launch."""
+    here unless given); balanced=False runs the plain launch. q_scaled: the
+    queries carry the factor log2(e)/sqrt(128) (qkv_rope(..., q_scaled=True)),
+    the kernel the block runs."""
     import torch
     B, T = q_r.shape[:2]
     kv_len = k_r.shape[1]
@@ -396,7 +404,7 @@ def attention(q_r, k_r, v, *, causal: bool = True, mask=None, h_out=None, worksp
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().gqa_attention(_ptr(q_r), _ptr(k_r), _ptr(v), _ptr(mask), int(bool(causal)),
                                B, T, kv_len, _ptr(h_out), _ptr(workspace), wsb,
-                               _stream(stream))
+                               int(bool(q_scaled)), _stream(stream))
     _check("gqa_attention", st)
     return h_out
 

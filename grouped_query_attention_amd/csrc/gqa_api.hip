@@ -408,8 +408,9 @@ size_t gqa_decode_workspace_bytes(int B, int S_max) {
 
 int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                  const gqa_bf16* w_v, const float* rope, int B, int T, gqa_bf16* q_r,
-                 gqa_bf16* k_r, gqa_bf16* v, void* stream) {
+                 gqa_bf16* k_r, gqa_bf16* v, int q_scaled, void* stream) {
   if (!x || !rope || !q_r || !k_r || !v || !w_q || !w_k || !w_v) return GQA_ERR_NULL;
+  if (q_scaled != 0 && q_scaled != 1) return GQA_ERR_ARG;
   if (!tokens_ok(B, T)) return GQA_ERR_SHAPE;
   if (misaligned(x) || misaligned(rope) || misaligned(q_r) || misaligned(k_r) ||
       misaligned(v) || misaligned(w_q) || misaligned(w_k) || misaligned(w_v))
@@ -417,15 +418,17 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
   const long long M = (long long)B * T;
   return hip_status(gqa::launch_qkv_rope(x, w_q, w_k, w_v, rope, (int)M, T, q_r,
                                          (long long)T * D_MODEL, D_MODEL, k_r, v,
-                                         (long long)T * KV_W, KV_W, nullptr, 1.0f,
+                                         (long long)T * KV_W, KV_W, nullptr,
+                                         q_scaled ? gqa::QK_SCALE_LOG2 : 1.0f,
                                          (hipStream_t)stream));
 }
 
 int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
                   const float* mask, int causal, int B, int T, int kv_len, gqa_bf16* h_out,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, int q_scaled, void* stream) {
   if (!q_r || !k_r || !v || !h_out) return GQA_ERR_NULL;
   if (causal != 0 && causal != 1) return GQA_ERR_ARG;
+  if (q_scaled != 0 && q_scaled != 1) return GQA_ERR_ARG;
   if (causal && mask) return GQA_ERR_ARG;
   if (!tokens_ok(B, T) || kv_len < 1) return GQA_ERR_SHAPE;
   if (kv_len != T) return GQA_ERR_UNSUPPORTED;
@@ -436,8 +439,8 @@ int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
   if (workspace && workspace_bytes < need) return GQA_ERR_WORKSPACE;
   float* part = workspace && need ? static_cast<float*>(workspace) : nullptr;
   return hip_status(gqa::launch_flash_attention(q_r, k_r, v, (long long)kv_len * KV_W, mask,
-                                                causal, B, T, kv_len, 0, h_out, part, false,
-                                                (hipStream_t)stream));
+                                                causal, B, T, kv_len, 0, h_out, part,
+                                                q_scaled != 0, (hipStream_t)stream));
 }
 
 int gqa_output_projection(const gqa_bf16* h, const gqa_bf16* w_o, int M, float* out,

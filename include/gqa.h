@@ -288,10 +288,13 @@ int gqa_mlp_forward_prenorm(const gqa_bf16* h, const gqa_bf16* norm_w, float eps
  * rounded to bf16 once, after the rotation.
  *   x [B][T][4096], w_q, w_k, w_v, rope [T][64][2] as above
  *   q_r [B][T][32][128], k_r [B][T][8][128], v [B][T][8][128]   bf16 out
+ *   q_scaled   0: q_r holds Q_r; 1: q_r holds Q_r times log2(e)/sqrt(128) (the
+ *              softmax's score scale in base 2, rounded once with it), the form
+ *              the block and chunk entries hand to their attention stage
  */
 int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                  const gqa_bf16* w_v, const float* rope, int B, int T,
-                 gqa_bf16* q_r, gqa_bf16* k_r, gqa_bf16* v, void* stream);
+                 gqa_bf16* q_r, gqa_bf16* k_r, gqa_bf16* v, int q_scaled, void* stream);
 
 /*
  * Workspace bytes gqa_attention uses to balance a causal launch with few query
@@ -310,10 +313,15 @@ size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal);
  *   workspace   NULL (plain launch), or >= gqa_attention_workspace_bytes(B, T,
  *               kv_len, causal) bytes of device memory (balanced launch; the
  *               result is the same up to fp32 summation order)
+ *   q_scaled    0: q_r is Q_r; 1: q_r is Q_r times log2(e)/sqrt(128), as
+ *               gqa_qkv_rope writes it with q_scaled = 1 (the kernel the block
+ *               and chunk entries run: it spends no instruction on the scale)
+ * Returns GQA_ERR_ARG for q_scaled other than 0 or 1.
  */
 int gqa_attention(const gqa_bf16* q_r, const gqa_bf16* k_r, const gqa_bf16* v,
                   const float* mask, int causal, int B, int T, int kv_len,
-                  gqa_bf16* h_out, void* workspace, size_t workspace_bytes, void* stream);
+                  gqa_bf16* h_out, void* workspace, size_t workspace_bytes, int q_scaled,
+                  void* stream);
 
 /*
  * Stage 3 alone: Δ = H·W_O (Merge and project page, Explanation; "All 13

@@ -231,16 +231,18 @@ def test_balanced_plan_partials_at_t2048():
 
 def test_stage_entries_reject():
     lib = gqa.lib()
-    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, None) == SHAPE
-    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, None, FAKE, 1, 4, FAKE, FAKE, FAKE, None) == NULL
-    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, MIS, FAKE, FAKE, None) == ALIGN
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 4, FAKE, None, 0, None) == ARG
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 4, 5, FAKE, None, 0, None) == UNSUPPORTED
-    assert lib.gqa_attention(FAKE, FAKE, None, None, 1, 1, 4, 4, FAKE, None, 0, None) == NULL
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, MIS, 1 << 30,
+    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 0, FAKE, FAKE, FAKE, 0, None) == SHAPE
+    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, None, FAKE, 1, 4, FAKE, FAKE, FAKE, 0, None) == NULL
+    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, MIS, FAKE, FAKE, 0, None) == ALIGN
+    assert lib.gqa_qkv_rope(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 4, FAKE, FAKE, FAKE, 2, None) == ARG
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, FAKE, 1, 1, 4, 4, FAKE, None, 0, 0, None) == ARG
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 4, 4, FAKE, None, 0, 3, None) == ARG
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 4, 5, FAKE, None, 0, 0, None) == UNSUPPORTED
+    assert lib.gqa_attention(FAKE, FAKE, None, None, 1, 1, 4, 4, FAKE, None, 0, 0, None) == NULL
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, MIS, 1 << 30, 0,
                              None) == ALIGN
     need = gqa.attention_workspace_bytes(1, 2048, 2048, True)
-    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, FAKE, need - 1,
+    assert lib.gqa_attention(FAKE, FAKE, FAKE, None, 1, 1, 2048, 2048, FAKE, FAKE, need - 1, 1,
                              None) == WORKSPACE
     assert lib.gqa_output_projection(FAKE, FAKE, 0, FAKE, None) == SHAPE
     assert lib.gqa_output_projection(FAKE, MIS, 3, FAKE, None) == ALIGN

@@ -88,6 +88,59 @@ def test_qkv_rope_stage_wide_tiles_sampled(T):
     assert_close(bf16_to_np_f64(v[0, sel]), want_v, rel=STAGE_REL, what=f"V T={T}")
 
 
+def test_qkv_rope_stage_scaled_queries():
+    # q_scaled: the queries come out multiplied by log2(e)/sqrt(128) before their
+    # one rounding; keys and values are unchanged bit for bit
+    B, T = 2, 200
+    print(f"[case] qkv_rope q_scaled B={B} T={T}", flush=True)
+    inp = gi.make_block_inputs(140, B, T)
+    x = to_dev_bf16(inp.x)
+    wq, wk, wv, _ = _weights(inp)
+    q0, k0, v0 = gqa.qkv_rope(x, wq, wk, wv, _rope(T))
+    q1, k1, v1 = gqa.qkv_rope(x, wq, wk, wv, _rope(T), q_scaled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(k0, k1) and torch.equal(v0, v1)
+    ref = O.block_forward(inp.x, inp.wq, inp.wk, inp.wv, inp.wo, 32, 8)
+    c = np.log2(np.e) / np.sqrt(128.0)
+    assert_close(bf16_to_np_f64(q1), ref["q_r"] * c, rel=STAGE_REL, mabs=STAGE_REL,
+                 what="log2(e)/sqrt(128) Q_r")
+
+
+@pytest.mark.parametrize("B,T,causal", [(1, 300, True), (2, 200, False), (1, 1000, True)])
+def test_attention_stage_scaled_queries(B, T, causal):
+    # queries given times log2(e)/sqrt(128); the oracle takes the exact
+    # pre-scaled bf16 values divided by that factor
+    print(f"[case] attention q_scaled B={B} T={T} causal={causal}", flush=True)
+    q, k, v = _qkv_direct(900 + T, B, T)
+    c = np.log2(np.e) / np.sqrt(128.0)
+    qs = gi.f32_to_bf16_bits((O.bf16_to_f64(q) * c).astype(np.float32))
+    h = gqa.attention(to_dev_bf16(qs), to_dev_bf16(k), to_dev_bf16(v), causal=causal,
+                      q_scaled=True)
+    torch.cuda.synchronize()
+    mask = O.causal_mask(T) if causal else None
+    want = O.grouped_attention(O.bf16_to_f64(qs) / c, O.bf16_to_f64(k), O.bf16_to_f64(v), mask)
+    assert_close(bf16_to_np_f64(h), want, rel=STAGE_REL, what="H (scaled queries)")
+
+
+@pytest.mark.parametrize("B,T", [(2, 300), (1, 1000)])
+def test_stage_entries_with_scaled_queries_reproduce_the_block(B, T):
+    # above 256 tokens the block runs exactly the kernels of its three stage
+    # entries (q_scaled = 1; the balanced attention plan at T = 1000): same bits
+    print(f"[case] stages vs block B={B} T={T}", flush=True)
+    inp = gi.make_block_inputs(150 + T, B, T)
+    x = to_dev_bf16(inp.x)
+    wq, wk, wv, wo = _weights(inp)
+    rope = _rope(T)
+    hb = torch.empty((B, T, 32, 128), dtype=torch.bfloat16, device=dev())
+    out = gqa.block_forward(x, wq, wk, wv, wo, rope, causal=True, h_out=hb)
+    q, k, v = gqa.qkv_rope(x, wq, wk, wv, rope, q_scaled=True)
+    h = gqa.attention(q, k, v, causal=True, q_scaled=True)
+    o2 = gqa.output_projection(h, wo).view(B, T, 4096)
+    torch.cuda.synchronize()
+    assert torch.equal(h, hb)
+    assert torch.equal(o2, out)
+
+
 # M = 3000: 128x256 tiles with a ragged last token tile; 4096 and 4100: 256x256
 # tiles (the second with a ragged last tile)
 @pytest.mark.parametrize("M", [1, 300, 1024, 3000, 4096, 4100])
