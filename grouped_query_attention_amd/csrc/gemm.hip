@@ -42,6 +42,8 @@
 // a fixed order (deterministic) and applies the epilogue (rotation + bf16,
 // or fp32 store).
 
+#include <type_traits>
+
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -245,14 +247,16 @@ void gemm_nt_kernel(GemmArgs a) {
     src[j] = rowp + (size_t)k_first * BK + lc * 8;
   }
   const uint32_t lds0 = lds_addr(smem);
+  // load instruction j of this wave for step kt into ring stage `stage`
+  auto issue_one = [&](int kt, int stage, int j) {
+    const int i = wave + j * C::NW;
+    const uint32_t dst = lds0 + 2u * (uint32_t)(stage * C::STAGE_ELEMS + i * 512);
+    if (C::NT_W && (j < C::NJ_P) == C::SWAP) dma16_nt((const void*)(src[j] + kt * BK), dst);   // weight rows
+    else dma16((const void*)(src[j] + kt * BK), dst);
+  };
   auto issue = [&](int kt, int stage) {
 #pragma unroll
-    for (int j = 0; j < C::NI_W; ++j) {
-      const int i = wave + j * C::NW;
-      const uint32_t dst = lds0 + 2u * (uint32_t)(stage * C::STAGE_ELEMS + i * 512);
-      if (C::NT_W && (j < C::NJ_P) == C::SWAP) dma16_nt((const void*)(src[j] + kt * BK), dst);   // weight rows
-      else dma16((const void*)(src[j] + kt * BK), dst);
-    }
+    for (int j = 0; j < C::NI_W; ++j) issue_one(kt, stage, j);
   };
 
   f32x4 acc[NP][NQ];
@@ -269,13 +273,24 @@ void gemm_nt_kernel(GemmArgs a) {
   // fragments double-buffered in registers: reads of slice kk+1 overlap the MFMAs
   // of kk (declared outside the step loop: the generated loop is faster)
   u32x4 af[2][NP], bf[2][NQ];
-  auto read_frags = [&](const uint16_t* sp, int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
+  // after_read(r) runs after fragment read r (0 .. NP+NQ-1) in program order
+  auto read_frags_then = [&](const uint16_t* sp, int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ],
+                             auto&& after_read) {
     const uint16_t* sq = sp + PR * BK;
     const int ch = kk * 4 + lg;
 #pragma unroll
-    for (int i = 0; i < NP; ++i) fa[i] = ld16(sp + swz<BK>(wp * C::WP + i * 16 + l16, ch));
+    for (int i = 0; i < NP; ++i) {
+      fa[i] = ld16(sp + swz<BK>(wp * C::WP + i * 16 + l16, ch));
+      after_read(i);
+    }
 #pragma unroll
-    for (int j = 0; j < NQ; ++j) fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 16 + l16, ch));
+    for (int j = 0; j < NQ; ++j) {
+      fb[j] = ld16(sq + swz<BK>(wq * C::WQ + j * 16 + l16, ch));
+      after_read(NP + j);
+    }
+  };
+  auto read_frags = [&](const uint16_t* sp, int kk, u32x4 (&fa)[NP], u32x4 (&fb)[NQ]) {
+    read_frags_then(sp, kk, fa, fb, [](int) {});
   };
   auto mfmas = [&](int kk) {
 #pragma unroll
@@ -315,18 +330,37 @@ void gemm_nt_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    for (int kt = 0; kt < NK - 1; ++kt) {
+    // Step kt: slices 0 .. NS-2, the wait and barrier, then the last slice
+    // with the next step's first fragment reads between its MFMAs. While
+    // steps remain to be loaded, the refill of the stage just finished goes
+    // out one load instruction after each of those reads rather than as a
+    // block after the barrier, so no wave stalls on issuing its loads before
+    // its first MFMA (QKV 2-3 % faster at M = 2048 and 32768). The two loops
+    // keep the refill decision out of the loop body (a branch there splits
+    // the scheduling region and the accumulators' registers).
+    auto step = [&](int kt, auto refill) {
       body(smem + (kt % STAGES) * C::STAGE_ELEMS);
       __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters free (gfx9 encoding)
       wait_keep<C::NI_W, STAGES - 2>(min(STAGES - 2, NK - 2 - kt));
       barrier_no_fence();
-      // every wave is done with stage kt % STAGES: refill it with step kt + STAGES
-      if (kt + STAGES < NK) issue(kt + STAGES, kt % STAGES);
-      read_frags(smem + ((kt + 1) % STAGES) * C::STAGE_ELEMS, 0, af[NS & 1], bf[NS & 1]);
+      const uint16_t* next = smem + ((kt + 1) % STAGES) * C::STAGE_ELEMS;
+      if constexpr (decltype(refill)::value) {
+        // every wave is done with stage kt % STAGES: refill it with step kt + STAGES
+        read_frags_then(next, 0, af[NS & 1], bf[NS & 1], [&](int r) {
+          if (r < C::NI_W) issue_one(kt + STAGES, kt % STAGES, r);
+        });
+#pragma unroll
+        for (int j = NP + NQ; j < C::NI_W; ++j) issue_one(kt + STAGES, kt % STAGES, j);
+      } else {
+        read_frags(next, 0, af[NS & 1], bf[NS & 1]);
+      }
       mfmas(NS - 1);
       spread();
       __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    int kt = 0;
+    for (; kt < NK - STAGES; ++kt) step(kt, std::true_type{});
+    for (; kt < NK - 1; ++kt) step(kt, std::false_type{});
     body(smem + ((NK - 1) % STAGES) * C::STAGE_ELEMS);
     mfmas(NS - 1);
   } else {
