@@ -17,9 +17,11 @@
 // the lane 32 away, and the bf16 probabilities feed the P·V MFMA straight from
 // the score accumulator. V is read with transposing LDS loads, in the key
 // order the accumulator holds. The softmax is the online (running max /
-// running sum) form in base 2 with log2(e)/sqrt(128) folded into one
-// multiply-add, with a lazily moved reference max; the division by the row sum
-// happens once, at the end, in fp32.
+// running sum) form in base 2 with a lazily moved reference max; the factor
+// log2(e)/sqrt(128) is either folded into one multiply-add per score or, in
+// the block paths, carried by the queries themselves (the QKV epilogue
+// applies it), whose score MFMA chain then starts from minus the row's
+// reference. The division by the row sum happens once, at the end, in fp32.
 //
 // Decode (decode_splitkv_kernel + decode_merge_kernel): the key range of each
 // sequence is split into chunks; persistent workgroups of 4 waves (one per KV
@@ -148,7 +150,6 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   const uint16_t* vbase = a.v + b * a.kv_bstride + g * D_HEAD;
 
   u32x4 qf[8];
-
 
   // Direct-to-LDS loads of tile t: instruction i (0..31) covers rows 4(i&15)..+3
   // of K (i < 16) or V; lane l writes row 4(i&15) + (l >> 4), physical chunk
