@@ -78,15 +78,18 @@ struct GemmArgs {
 };
 
 // Chunk permutation of row r for LDS rows of KB bf16 (KB/8 chunks of 16 bytes).
-// The 16 lanes of a fragment read take one chunk c of 16 consecutive rows and
-// must hit the 16 distinct 16-byte slots of a 256-byte bank window.
-//  * KB = 64 (128-byte rows, 2 per window): a bijection on r & 7 for any 8
-//    aligned rows that also differs between rows r and r + 8.
-//  * KB = 32 (64-byte rows, 4 per window): rows r mod 4 fill the window's four
-//    64-byte quarters and (r >> 2) & 3 picks the chunk inside each.
+// The 16 lanes of a fragment read take one chunk c of 16 consecutive rows.
+//  * KB = 64 (128-byte rows): chunk c at c ^ (r & 7). Measured with the LDS
+//    counters on the 16x16x32 fragment pattern (a probe reading every
+//    candidate layout): 4 active LDS cycles per ds_read_b128 and no bank
+//    conflicts, where c ^ (r & 7) ^ ((r >> 3) & 1) (conflict-free for the
+//    32-row fragments of 32x32x16 MFMAs) took 8, half of them conflicts, and
+//    no permutation 16.
+//  * KB = 32 (64-byte rows, 4 per 256-byte window): rows r mod 4 fill the
+//    window's four 64-byte quarters and (r >> 2) & 3 picks the chunk inside each.
 template <int KB>
 __device__ __forceinline__ int rperm(int r) {
-  if constexpr (KB == 64) return (r & 7) ^ ((r >> 3) & 1);
+  if constexpr (KB == 64) return r & 7;
   else return (r >> 2) & 3;
 }
 template <int KB>
