@@ -234,6 +234,36 @@ def test_attention_window_mask_rows_start_late():
                                mask.astype(np.float64))
     assert_close(got, want, rel=STAGE_REL, what="H (window mask)")
 
+@pytest.mark.parametrize("q_scaled", [False, True])
+def test_attention_fully_masked_rows_give_zero(q_scaled):
+    # A row whose every key the caller's mask removes has no defined softmax
+    # (reading 9): the kernels write H = 0 for it (include/gqa.h), and every
+    # other row still matches the oracle. Rows 0, 63, 64 and 199 sit at tile
+    # edges and the ragged end of T = 200.
+    B, T = 2, 200
+    print(f"[case] attention fully masked rows B={B} T={T} q_scaled={q_scaled}", flush=True)
+    q, k, v = _qkv_direct(414, B, T)
+    rng = np.random.Generator(np.random.PCG64(415))
+    mask = rng.standard_normal((T, T)).astype(np.float32)
+    mask[rng.random((T, T)) < 0.3] = -np.inf
+    mask[:, 0] = 0.0
+    dead = np.array([0, 5, 63, 64, 130, 199])
+    mask[dead, :] = -np.inf
+    c = np.log2(np.e) / np.sqrt(128.0)
+    qd = gi.f32_to_bf16_bits((O.bf16_to_f64(q) * c).astype(np.float32)) if q_scaled else q
+    h = gqa.attention(to_dev_bf16(qd), to_dev_bf16(k), to_dev_bf16(v), causal=False,
+                      mask=to_dev_f32(mask), q_scaled=q_scaled)
+    torch.cuda.synchronize()
+    got = bf16_to_np_f64(h)
+    assert np.all(got[:, dead] == 0.0), "fully masked rows must be exactly zero"
+    live = np.setdiff1d(np.arange(T), dead)
+    ok_mask = mask.copy()
+    ok_mask[dead, :] = 0.0                              # any defined row; not compared
+    qo = O.bf16_to_f64(qd) / c if q_scaled else O.bf16_to_f64(q)
+    want = O.grouped_attention(qo, O.bf16_to_f64(k), O.bf16_to_f64(v), ok_mask.astype(np.float64))
+    assert_close(got[:, live], want[:, live], rel=STAGE_REL, what="H (live rows)")
+
+
 # --- whole block ---------------------------------------------------------------------
 
 # (2, 30): 60 tokens take the projections' split-reduction path with 64-token
