@@ -153,22 +153,18 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
 
   // Direct-to-LDS loads of tile t: instruction i (0..31) covers rows 4(i&15)..+3
   // of K (i < 16) or V; lane l writes row 4(i&15) + (l >> 4), physical chunk
-  // l & 15. Keys past the end are clamped to the last key (finite values; masked).
-  // This lane's source for instruction j at tile 0; a whole tile adds a uniform
-  // offset, and only a tile reaching past the last key takes the clamped path.
-  // the wave index as a scalar for the load addresses only: the per-lane form
-  // above keeps the lagging waves' branch the way the step loop is fastest
+  // l & 15. Wave w issues instructions i = w + 8j, j = 0..3: K for j < 2, V
+  // for j >= 2, and row rr + 32(j & 1) with rr = 4w + (lane >> 4), whose
+  // chunk swizzle is the same for j and j + 1. So the lane's part of each
+  // source address is one of two loop-invariant byte offsets, and a tile adds
+  // only a wave-uniform base (scalar arithmetic). Keys past the end are
+  // clamped to the last key (finite values; masked); only a tile reaching past
+  // the last key takes that path.
   const int wave_u = wave_id();
   const uint32_t lds0 = lds_addr(smem);
-  const uint16_t* src0[FA_NI_W];
-#pragma unroll
-  for (int j = 0; j < FA_NI_W; ++j) {
-    const int i = wave_u + 8 * j;
-    const bool isv = i >= 16;
-    const int r = 4 * (i & 15) + (lane >> 4);
-    const int lc = isv ? ((lane & 15) ^ ((r & 3) << 2)) : ((lane & 15) ^ (r & 15));
-    src0[j] = (isv ? vbase : kbase) + (size_t)r * (N_KV * D_HEAD) + lc * 8;
-  }
+  const int rr = 4 * wave_u + (lane >> 4);
+  const uint32_t voffK = (uint32_t)(rr * (N_KV * D_HEAD) + (((lane & 15) ^ (rr & 15)) << 3)) * 2u;
+  const uint32_t voffV = (uint32_t)(rr * (N_KV * D_HEAD) + (((lane & 15) ^ ((rr & 3) << 2)) << 3)) * 2u;
   auto issue = [&](int t) {
     const uint32_t st = lds0 + 2u * (uint32_t)((t % FA_STAGES) * 2 * FA_TILE);
     if (t * FA_BN + FA_BN <= a.kv_len) {
@@ -176,16 +172,17 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
 #pragma unroll
       for (int j = 0; j < FA_NI_W; ++j) {
         const int i = wave_u + 8 * j;
-        dma16((const void*)(src0[j] + toff), st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+        const uint16_t* sb = (j < 2 ? kbase : vbase) + toff + (size_t)(j & 1) * 32 * (N_KV * D_HEAD);
+        dma16_sv(sb, j < 2 ? voffK : voffV, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     } else {
 #pragma unroll
       for (int j = 0; j < FA_NI_W; ++j) {
         const int i = wave_u + 8 * j;
-        const int r = 4 * (i & 15) + (lane >> 4);
-        const int key = min(t * FA_BN + r, a.kv_len - 1);
-        const uint16_t* src = src0[j] + (ptrdiff_t)(key - r) * (N_KV * D_HEAD);
-        dma16((const void*)src, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+        const int key = min(t * FA_BN + rr + 32 * (j & 1), a.kv_len - 1);
+        // byte offset of (key, chunk) from the sequence's base: never negative
+        const uint32_t vo = (j < 2 ? voffK : voffV) + (uint32_t)((key - rr) * (N_KV * D_HEAD)) * 2u;
+        dma16_sv(j < 2 ? kbase : vbase, vo, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     }
   };

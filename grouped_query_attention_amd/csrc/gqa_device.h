@@ -89,6 +89,14 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_byte) {
                :: "v"(src), "s"(lds_byte) : "memory");
 }
 
+// dma16 from a wave-uniform 64-bit base (SGPR pair) plus a per-lane 32-bit
+// byte offset: a tile's loads then need no per-lane address arithmetic, only
+// scalar adds to the base.
+__device__ __forceinline__ void dma16_sv(const void* sbase, uint32_t voff, uint32_t lds_byte) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_byte) : "memory");
+}
+
 // dma16 with the non-temporal hint, for data that is read exactly once (the
 // decode kernel's K/V cache stream): the lines are not kept in L2 and the
 // Infinity Cache. A 2.1 GB single-pass stream runs 13 % faster this way
