@@ -176,13 +176,15 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         dma16_sv(sb, j < 2 ? voffK : voffV, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     } else {
+      const size_t toff = (size_t)t * FA_BN * (N_KV * D_HEAD);
 #pragma unroll
       for (int j = 0; j < FA_NI_W; ++j) {
         const int i = wave_u + 8 * j;
         const int key = min(t * FA_BN + rr + 32 * (j & 1), a.kv_len - 1);
-        // byte offset of (key, chunk) from the sequence's base: never negative
-        const uint32_t vo = (j < 2 ? voffK : voffV) + (uint32_t)((key - rr) * (N_KV * D_HEAD)) * 2u;
-        dma16_sv(j < 2 ? kbase : vbase, vo, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
+        // byte offset of (key, chunk) from the tile's first row: in [0, 128 KiB)
+        // (the tile starts before the last key), whatever the sequence length
+        const uint32_t vo = (j < 2 ? voffK : voffV) + (uint32_t)((key - t * FA_BN - rr) * (N_KV * D_HEAD)) * 2u;
+        dma16_sv((j < 2 ? kbase : vbase) + toff, vo, st + 2u * (uint32_t)((i >= 16 ? FA_TILE : 0) + (i & 15) * 512));
       }
     }
   };
