@@ -22,6 +22,10 @@
 // the block paths, carried by the queries themselves (the QKV epilogue
 // applies it), whose score MFMA chain then starts from minus the row's
 // reference. The division by the row sum happens once, at the end, in fp32.
+// Causal launches with too few query tiles to fill the chip follow a host-made
+// plan that cuts the key-tile stream of each (sequence, KV head) into bins of
+// equal cost (flash_plan.h); flash_merge_kernel combines the pieces of cut
+// query tiles.
 //
 // Decode (decode_splitkv_kernel + decode_merge_kernel): the key range of each
 // sequence is split into chunks; persistent workgroups of 4 waves (one per KV
@@ -31,6 +35,7 @@
 // decode_plan.h.
 
 #include "decode_plan.h"
+#include "flash_plan.h"
 #include "gqa_device.h"
 #include "gqa_launch.h"
 
@@ -46,8 +51,6 @@ constexpr float NEG_INF = -__builtin_inff();
 // Prefill
 // ----------------------------------------------------------------------------
 
-constexpr int FA_BQ = 64;        // query positions per workgroup
-constexpr int FA_BN = 64;        // keys per staged tile
 constexpr int FA_THREADS = 512;  // 8 waves: 4 heads x 2 blocks of 32 positions
 constexpr int FA_STAGES = 4;     // K/V tiles resident: t-1 (V, lagging waves), t, t+1, t+2
 constexpr int FA_TILE = FA_BN * D_HEAD;   // elements of one K or V tile (16 KiB)
@@ -78,26 +81,8 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Causal work balance. With few query tiles (B * 8 * tiles under two per CU),
-// the longest workgroup (the last query tile attends to every key tile) sets
-// the time: at T = 2048 it does 32 key tiles while the mean is 16.5. Such
-// launches are planned on the host, stream-K style: per (sequence, KV head)
-// the query tiles are laid out in the order last, first, second-to-last,
-// second, ... (so a long tile is followed by a short one), their key tiles are
-// concatenated, and the stream is cut into bins of equal cost (key tiles plus a
-// fixed overhead per piece); workgroup (bin, b, g) runs the pieces of its bin
-// one after the other. A query tile cut across two
-// bins is computed in pieces; a piece writes an unnormalised fp32 partial
-// (O, running max, running sum) per query row, and flash_merge_kernel
-// combines the pieces of each cut tile, exactly as the online softmax
-// combines key tiles.
-constexpr int FA_MAX_ENT = 256;    // (query tile, key range) entries of a plan
-constexpr int FA_MAX_BINS = 256;   // bins per (sequence, KV head)
-constexpr int FA_MAX_MERGE = 128;  // cut query tiles of a plan
-constexpr int FA_PLAN_CUS = 256;   // CUs the plan balances over (MI355X)
-constexpr int FA_MIN_PIECE = 4;    // key tiles: bins never hold fewer
-constexpr int FA_ENTRY_COST = 4;   // key-tile trips an entry costs beyond its tiles (plan balance)
-constexpr int FA_DIRECT = 255;     // slot value of an entry that writes H itself
+// Causal launches with few query tiles run a host-made plan (flash_plan.h).
+
 // Partial of one piece for one (sequence, KV head): O[4 heads][64 rows][128],
 // then max[4][64] (base-2 units: the score times log2(e)/sqrt(128)), then
 // sum[4][64], fp32.
@@ -454,7 +439,7 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
 // and summed, then divided by the summed row sums (pieces in slot order). The
 // pieces' maxima are in base-2 units.
 __global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
-  constexpr int MAXP = 4;
+  constexpr int MAXP = FA_MERGE_MAXP;
   const int g = blockIdx.x & (N_KV - 1);
   int rest = blockIdx.x >> 3;
   const int b = rest % a.B;
@@ -499,127 +484,9 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
                                           pack_bf16x2(acc[2] * inv, acc[3] * inv)};
 }
 
-namespace {
-
-constexpr int FA_MERGE_MAXP = 4;   // pieces per cut query tile (flash_merge_kernel)
-
-struct FlashPlan {
-  int n_bins = 0, n_ent = 0, n_merge = 0, n_slots = 0;
-  unsigned short bin_start[FA_MAX_BINS + 1];
-  unsigned ent[FA_MAX_ENT];
-  unsigned mrg[FA_MAX_MERGE];
-};
-
-// Key tiles of query tile qt (causal).
-inline int flash_key_tiles(int qt, int kv_len, int q_pos0) {
-  const int kv_end = min(kv_len, q_pos0 + (qt + 1) * FA_BQ);
-  return (kv_end + FA_BN - 1) / FA_BN;
-}
-
-// Plans a causal launch with too few query tiles to balance; returns false
-// (plain launch) when no plan applies or it would not fit its tables.
-bool flash_plan(int B, int T, int kv_len, int q_pos0, int causal, FlashPlan& p) {
-  p = FlashPlan{};
-  if (!causal) return false;
-  const int nq = (T + FA_BQ - 1) / FA_BQ;
-  if ((long long)B * N_KV * nq >= 2LL * FA_PLAN_CUS || nq > 255) return false;
-  // zigzag order of query tiles and the unit (key tile) stream per (b, g)
-  int order[256], len[256];
-  long long U = 0;
-  int longest = 0;
-  for (int i = 0; i < nq; ++i) {
-    order[i] = (i & 1) ? i / 2 : nq - 1 - i / 2;
-    len[i] = flash_key_tiles(order[i], kv_len, q_pos0);
-    U += len[i];
-    longest = max(longest, len[i]);
-  }
-  if (longest > 255) return false;
-  int bins = FA_PLAN_CUS / (B * N_KV);
-  if ((long long)bins > U / FA_MIN_PIECE) bins = (int)(U / FA_MIN_PIECE);
-  bins = min(bins, FA_MAX_BINS);
-  if (bins < 2) return false;
-  // worth it only when the longest tile exceeds a bin by a quarter or more
-  // (a chunk of 2048 positions after 2048 cached ones: 64 key tiles against a
-  // mean of 48.5 per bin; the whole chunk step 314 -> 306 us)
-  if (4 * (long long)longest * bins < 5 * U) return false;
-  // Bins are filled greedily in stream order up to a cost T, where an entry
-  // costs its key tiles plus FA_ENTRY_COST (the wait for its queries and first
-  // tiles, its output write and the re-synchronisation of the waves); T is the
-  // smallest cost at which the stream fits in `bins` bins (feasibility is
-  // monotone in T, so it is found by bisection). fill returns the number of
-  // entries at cost T (recording the first `cap`: key tiles taken and bin), or
-  // -1 when the stream does not fit.
-  auto fill = [&](long long T, int cap, int* take_out, int* bin_out) -> int {
-    int qi = 0, kt = 0, n = 0;
-    for (int s = 0; s < bins && qi < nq; ++s) {
-      long long cost = 0;
-      while (qi < nq && cost + FA_ENTRY_COST + 1 <= T) {
-        const long long room = T - cost - FA_ENTRY_COST;
-        const int take = len[qi] - kt < room ? len[qi] - kt : (int)room;
-        if (n < cap) { take_out[n] = take; bin_out[n] = s; }
-        ++n;
-        cost += FA_ENTRY_COST + take;
-        kt += take;
-        if (kt == len[qi]) { ++qi; kt = 0; }
-      }
-    }
-    return qi == nq ? n : -1;
-  };
-  long long lo = (U + bins - 1) / bins, hi = U + FA_ENTRY_COST;   // one bin holds all at hi
-  while (lo < hi) {
-    const long long mid = (lo + hi) / 2;
-    if (fill(mid, 0, nullptr, nullptr) >= 0) hi = mid; else lo = mid + 1;
-  }
-  int take_of[FA_MAX_ENT], bin_of[FA_MAX_ENT];
-  const int n_ent = fill(lo, FA_MAX_ENT, take_of, bin_of);
-  if (n_ent < 0 || n_ent > FA_MAX_ENT) return false;
-  // pass 1: pieces per query tile; pass 2: entries, slots, merges
-  int pieces_of[256];
-  for (int pass = 0; pass < 2; ++pass) {
-    int qi = 0, kt = 0, n = 0;   // current query tile (order index), key tile; entry
-    int next_slot[256];
-    if (pass == 1) {
-      p.n_slots = 0;
-      for (int i = 0; i < nq; ++i) {
-        next_slot[i] = FA_DIRECT;
-        if (pieces_of[i] > 1) {
-          if (pieces_of[i] > FA_MERGE_MAXP || p.n_merge >= FA_MAX_MERGE) return false;
-          next_slot[i] = p.n_slots;
-          p.mrg[p.n_merge++] = (unsigned)order[i] | (unsigned)p.n_slots << 8 |
-                               (unsigned)pieces_of[i] << 16;
-          p.n_slots += pieces_of[i];
-        }
-      }
-      if (p.n_slots >= FA_DIRECT) return false;
-    } else {
-      for (int i = 0; i < nq; ++i) pieces_of[i] = 0;
-    }
-    for (int s = 0; s < bins; ++s) {
-      if (pass == 1) p.bin_start[s] = (unsigned short)p.n_ent;
-      while (n < n_ent && bin_of[n] == s) {
-        const int take = take_of[n++];
-        if (pass == 0) {
-          ++pieces_of[qi];
-        } else {
-          const int slot = next_slot[qi] == FA_DIRECT ? FA_DIRECT : next_slot[qi]++;
-          p.ent[p.n_ent++] = (unsigned)order[qi] | (unsigned)kt << 8 |
-                             (unsigned)(kt + take) << 16 | (unsigned)slot << 24;
-        }
-        kt += take;
-        if (kt == len[qi]) { ++qi; kt = 0; }
-      }
-    }
-    if (pass == 1) p.bin_start[bins] = (unsigned short)p.n_ent;
-  }
-  p.n_bins = bins;
-  return true;
-}
-
-}  // namespace
-
 size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal) {
   FlashPlan p;
-  if (!flash_plan(B, T, kv_len, q_pos0, causal, p)) return 0;
+  if (!flash_plan(B, T, kv_len, q_pos0, causal, N_KV, p)) return 0;
   return (size_t)p.n_slots * B * N_KV * FA_PART * sizeof(float);
 }
 
@@ -632,7 +499,7 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
   a.B = B; a.T = T; a.kv_len = kv_len; a.q_pos0 = q_pos0; a.causal = causal;
   a.n_qtiles = (T + FA_BQ - 1) / FA_BQ;
   FlashPlan plan;
-  const bool planned = partials && flash_plan(B, T, kv_len, q_pos0, causal, plan);
+  const bool planned = partials && flash_plan(B, T, kv_len, q_pos0, causal, N_KV, plan);
   long long grid = (long long)a.n_qtiles * B * N_KV;
   if (planned) {
     a.part = partials;
