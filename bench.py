@@ -501,6 +501,47 @@ class Bench:
         return {"stage": "attention", "ms": ms, "median_ms": med,
                 "TFLOP/s": F / (ms * 1e-3) / 1e12}
 
+    def vendor_gemm(self, M=32768, reps=8):
+        """Context only: the block's two projection stages at M tokens against
+        the vendor BLAS (torch.mm, hipBLASLt on ROCm) on the same operands,
+        alternated in one process so both see the same part and clock."""
+        torch, gqa = self.torch, self.gqa
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(5)
+        T = 4096
+        B = M // T
+
+        def rnd_bf16(shape, std):
+            return (torch.randn(shape, device=self.dev, generator=g) * std).to(torch.bfloat16)
+
+        x = rnd_bf16((B, T, 4096), 1.0)
+        wq, wk, wv, wo = (rnd_bf16((n, 4096), 0.02) for n in (4096, 1024, 1024, 4096))
+        wqkv = torch.cat([wq, wk, wv], 0).contiguous()
+        rope = torch.from_numpy(gqa.rope_table(np.arange(T))).to(self.dev)
+        h = rnd_bf16((M, 4096), 1.0)
+        x2 = x.view(M, 4096)
+        legs = [("qkv_rope (this library)", lambda: gqa.qkv_rope(x, wq, wk, wv, rope, q_scaled=True)),
+                ("x @ [W_Q;W_K;W_V]^T (torch.mm)", lambda: torch.mm(x2, wqkv.t())),
+                ("out_proj (this library)", lambda: gqa.output_projection(h, wo)),
+                ("H @ W_O^T (torch.mm)", lambda: torch.mm(h, wo.t()))]
+        times = {name: [] for name, _ in legs}
+        for it in range(reps + 1):
+            for name, fn in legs:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                torch.cuda.synchronize()
+                if it:
+                    times[name].append(e0.elapsed_time(e1))
+        for name, t in times.items():
+            t.sort()
+            ms = t[len(t) // 2]
+            F = 2 * M * 4096 * (6144 if "W_Q" in name or "qkv" in name else 4096)
+            print(json.dumps({"vendor_gemm": name, "M": M, "median_ms": round(ms, 5),
+                              "TFLOP/s": round(F / (ms * 1e-3) / 1e12, 1)}), flush=True)
+
     def calibrate_copy(self, mib):
         torch = self.torch
         n = mib << 20
@@ -525,6 +566,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="only run a plain device copy of MB mebibytes (3 times), for "
                          "scaling the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the projection stages at M = 32768 beside the vendor "
+                         "BLAS on the same operands (context, not a bench line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
@@ -534,6 +578,9 @@ def main():
     b = Bench(args)
     if args.calibrate_copy:
         b.calibrate_copy(args.calibrate_copy)
+        return
+    if args.vendor_gemm:
+        b.vendor_gemm()
         return
     extras = {"chunk": b.chunk, "prenorm": b.prenorm, "mlp": b.mlp}
     if args.only:
