@@ -21,7 +21,8 @@
 // kv_len is q_pos0 + T (a prefill chunk after q_pos0 cached positions).
 // <mode> "plan" checks the plan as made; "drop" first removes the last key
 // tile of the plan's last entry (or the entry itself), which every check run
-// must then flag. Prints one line per shape that breaks a rule and a final
+// must then flag; "info" also prints "info B T q_pos0 planned n_slots" per
+// shape. Prints one line per shape that breaks a rule and a final
 // "shapes N planned P broken M worst_ratio R" (R: costliest bin over the
 // plain launch's time, largest over planned shapes).
 #include <algorithm>
@@ -129,13 +130,16 @@ int main(int argc, char** argv) {
     return 2;
   }
   const bool drop = std::string_view(argv[1]) == "drop";
+  const bool info = std::string_view(argv[1]) == "info";
   long long shapes = 0, planned = 0, broken = 0;
   double worst = 0.0;
   auto one = [&](int B, int T, int q_pos0) {
     const int kv_len = q_pos0 + T;
     FlashPlan p;
     ++shapes;
-    if (!flash_plan(B, T, kv_len, q_pos0, 1, N_KV, p)) return;
+    const bool ok = flash_plan(B, T, kv_len, q_pos0, 1, N_KV, p);
+    if (info) std::printf("info %d %d %d %d %d\n", B, T, q_pos0, ok ? 1 : 0, ok ? p.n_slots : 0);
+    if (!ok) return;
     ++planned;
     if (drop) {
       unsigned& e = p.ent[p.n_ent - 1];

@@ -71,3 +71,27 @@ def test_a_missing_key_tile_is_flagged(walker):
     shapes, planned, broken, _, lines = _run(walker, "drop", "sweep", 64, 4200, 0, 333)
     assert planned > 1000
     assert broken == planned
+
+
+def test_library_sizes_the_same_plan(walker):
+    # the library's own compiled plan (through its workspace query) against the
+    # header the walker includes: planned exactly when the walker plans, with
+    # one fp32 partial per slot, sequence and KV head
+    gqa = pytest.importorskip("grouped_query_attention_amd")
+    try:
+        gqa.lib()
+    except Exception as e:   # library not built in this checkout
+        pytest.skip(f"libgqa not loadable: {e}")
+    shapes = [(1, 2048), (1, 1000), (1, 700), (1, 513), (1, 321), (2, 1024), (2, 300),
+              (3, 777), (1, 4032), (8, 4096), (1, 128), (4, 900), (7, 520)]
+    *_, lines = _run(walker, "info", *[v for B, T in shapes for v in (B, T, 0)])
+    got = {}
+    for ln in lines:
+        f = ln.split()
+        if f[0] == "info":
+            got[(int(f[1]), int(f[2]))] = (int(f[4]), int(f[5]))
+    part = 4 * 64 * 128 + 2 * 4 * 64   # floats per piece partial per (sequence, KV head)
+    for B, T in shapes:
+        planned, slots = got[(B, T)]
+        want = slots * B * 8 * part * 4 if planned else 0
+        assert gqa.attention_workspace_bytes(B, T, T, True) == want, (B, T)

@@ -163,9 +163,12 @@ def _qkv_direct(seed, B, T):
     return q, k, v
 
 
+# (1, 513) and (1, 700) run the balanced plan (cut query tiles, ragged last
+# tile); (1, 321) is a shape the plan declines because in its cost model the
+# cuts would make it slower than the plain launch
 @pytest.mark.parametrize("B,T,causal", [(1, 128, True), (2, 127, True), (1, 129, True),
                                         (2, 200, False), (1, 1, True), (1, 64, True),
-                                        (1, 513, True)])
+                                        (1, 513, True), (1, 700, True), (1, 321, True)])
 def test_attention_stage(B, T, causal):
     print(f"[case] attention B={B} T={T} causal={causal}", flush=True)
     q, k, v = _qkv_direct(300 + T, B, T)
