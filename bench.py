@@ -45,13 +45,13 @@ PARAMS_PER_BLOCK = 41_943_040  # W_Q + W_K + W_V + W_O
 # instantiation named here only: re-measure when it changes.
 PROFILED_TRAFFIC = {
     ("prefill_B1_T2048", "qkv_rope"): {"kernel": "gemm_nt_kernel<256, 192, 2, 4, 2, 0, 64>",
-                                       "bytes": 197.4e6},
+                                       "bytes": 197.3e6},
     ("prefill_B1_T2048", "attention"): {"kernel": "flash_fwd_kernel<true> + flash_merge_kernel",
-                                        "bytes": 102.2e6},
+                                        "bytes": 102.1e6},
     ("prefill_B1_T2048", "out_proj"): {"kernel": "gemm_nt_kernel<128, 256, 2, 4, 2, 1, 64>",
-                                       "bytes": 168.0e6},
+                                       "bytes": 167.9e6},
     ("prefill_B1_T131072", "attention"): {"kernel": "flash_fwd_kernel<true> (plain causal launch)",
-                                          "bytes": 19.596e9},
+                                          "bytes": 19.595e9},
 }
 
 HEADLINE = "prefill_B1_T131072"
