@@ -1,4 +1,5 @@
-"""GPU parity of a prefill chunk whose keys run past 2^21 cached positions.
+"""GPU parity of a prefill chunk and a decode step whose keys run past 2^21
+cached positions.
 
 Each cached key row of one sequence is 2 KiB (8 KV heads x 128 bf16), so from
 2^21 rows on a row's byte offset from the sequence base no longer fits in 32
@@ -108,3 +109,49 @@ def test_chunk_keys_past_two_million():
         print(f"[check] row {rows[ri]}: distance to the result without keys past 2^21 {d:.3f}",
               flush=True)
         assert d > 0.2
+
+
+def test_decode_step_past_two_million():
+    # one decode step of two sequences at position 2^21 + 36 in caches of
+    # 2^21 + 64 rows: the new key and value go into slot 2^21 + 36 (byte offset
+    # past 4 GiB from the sequence base), the second sequence starts 4 GiB
+    # into the cache, and with the cached rows below zero the new key carries H
+    B = 2
+    S_max = (1 << 21) + 64
+    start = (1 << 21) + 36
+    print(f"[case] decode B={B} S_max={S_max} start_pos={start}", flush=True)
+    inp = gi.make_block_inputs(2102, B, 1)
+    kc = torch.zeros((B, S_max, 8, 128), dtype=torch.bfloat16, device=dev())
+    vc = torch.zeros((B, S_max, 8, 128), dtype=torch.bfloat16, device=dev())
+    x = to_dev_bf16(inp.x[:, 0])
+    wq, wk, wv, wo = (to_dev_bf16(a) for a in (inp.wq, inp.wk, inp.wv, inp.wo))
+    rope = to_dev_f32(gqa.rope_table(np.arange(start, start + 1))[0])
+    hb = torch.empty((B, 32, 128), dtype=torch.bfloat16, device=dev())
+    gqa.decode_forward(x, wq, wk, wv, wo, rope, kc, vc, start, h_out=hb)
+    torch.cuda.synchronize()
+    h = bf16_to_np_f64(hb)                          # [B, 32, 128]
+    k_slot = bf16_to_np_f64(kc[:, start])           # [B, 8, 128]
+    v_slot = bf16_to_np_f64(vc[:, start])
+    del kc, vc
+    torch.cuda.empty_cache()
+
+    xs = O.bf16_to_f64(inp.x[:, 0])                 # [B, 4096]
+    cos, sin = O.rope_cos_sin([start], 128)
+    q_r = O.rope_rotate(O.split_heads(O.project(xs, O.bf16_to_f64(inp.wq)), 32)[:, None], cos, sin)[:, 0]
+    k_r = O.rope_rotate(O.split_heads(O.project(xs, O.bf16_to_f64(inp.wk)), 8)[:, None], cos, sin)[:, 0]
+    v = O.split_heads(O.project(xs, O.bf16_to_f64(inp.wv)), 8)
+    # the slot written past 4 GiB holds the new key and value (one bf16 rounding)
+    assert_close(k_slot, k_r, rel=3e-3, what="cache K slot past 2^21")
+    assert_close(v_slot, v, rel=3e-3, what="cache V slot past 2^21")
+    # H: start zero keys (score 0, value 0) and the new one; the decode path
+    # stores Q_r unscaled, rounded once to bf16
+    q_b, k_b, v_b = O.round_to_bf16(q_r), O.round_to_bf16(k_r), O.round_to_bf16(v)
+    want = np.empty((B, 32, 128))
+    for b in range(B):
+        for hd in range(32):
+            g = hd // 4
+            s_new = float(q_b[b, hd] @ k_b[b, g]) / math.sqrt(128)
+            # softmax over start zeros and s_new, weight of the new key
+            w = 1.0 / (1.0 + start * math.exp(-s_new))
+            want[b, hd] = w * v_b[b, g]
+    assert_close(h, want, rel=BLOCK_H_REL, mabs=BLOCK_H_ABS, what="decode H past 2^21 keys")
