@@ -104,6 +104,11 @@ struct FlashArgs {
   int n_bins;
   unsigned short bin_start[FA_MAX_BINS + 1];
   unsigned ent[FA_MAX_ENT];
+  // explicit mask with its tile classes (flash_mask_classes_kernel): class of
+  // (query tile qt, key tile t) at mcls[qt * nkp + t], rows padded to nkp (a
+  // multiple of 4) bytes; null: every tile mixed
+  const unsigned char* mcls;
+  int nkp;
 };
 
 struct FlashMergeArgs {
@@ -112,11 +117,71 @@ struct FlashMergeArgs {
   unsigned mrg[FA_MAX_MERGE];   // qtile | first slot << 8 | pieces << 16
 };
 
+// Explicit additive masks (the M of "All 13 steps") are classified per 64x64
+// tile before the attention launch: a tile whose in-range entries are all 0
+// adds nothing to the scores, one whose entries are all -inf removes its keys,
+// any other tile is added element by element. The attention then walks each
+// query tile's key tiles only from the first to the last tile that is not all
+// -inf (a causal or sliding-window mask passed explicitly costs what the
+// causal flag costs), skips the mask for all-zero tiles and loads it only for
+// mixed ones.
+constexpr unsigned char FA_MASK_ZERO = 0, FA_MASK_NEG_INF = 1, FA_MASK_MIXED = 2;
+
+// Workgroup (key tile t, query tile qt): 256 threads read the 64x64 tile and
+// agree on its class. vec (a 16-byte aligned mask whose rows are a multiple
+// of 4 floats): 16 bytes a lane (16 lanes per 256-byte row segment, 16 rows
+// per load instruction, the four loads of a lane issued before the first is
+// used); else one float a lane. Entries outside [T, kv_len] take part in
+// neither test.
+__global__ __launch_bounds__(256) void flash_mask_classes_kernel(const float* mask, int T,
+                                                                 int kv_len, int nkp, int vec,
+                                                                 unsigned char* cls) {
+  const int t = blockIdx.x, qt = blockIdx.y;
+  bool zero = true, ninf = true;
+  if (vec) {
+    const int col = t * FA_BN + 4 * (threadIdx.x & 15);
+    const int r0 = qt * FA_BQ + (threadIdx.x >> 4);
+    f32x4 x[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = r0 + 16 * i;
+      ok[i] = q < T && col < kv_len;
+      x[i] = ok[i] ? *reinterpret_cast<const f32x4*>(mask + (size_t)q * kv_len + col) : f32x4{};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (ok[i]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          zero = zero && x[i][j] == 0.f;
+          ninf = ninf && x[i][j] == NEG_INF;
+        }
+      }
+  } else {
+    const int col = t * FA_BN + (threadIdx.x & 63);
+    if (col < kv_len) {
+#pragma unroll 4
+      for (int r = threadIdx.x >> 6; r < FA_BQ; r += 4) {
+        const int q = qt * FA_BQ + r;
+        if (q >= T) break;
+        const float x = mask[(size_t)q * kv_len + col];
+        zero = zero && x == 0.f;
+        ninf = ninf && x == NEG_INF;
+      }
+    }
+  }
+  const int all_zero = __syncthreads_and(zero);
+  const int all_ninf = __syncthreads_and(ninf);
+  if (threadIdx.x == 0)
+    cls[(size_t)qt * nkp + t] = all_ninf ? FA_MASK_NEG_INF : all_zero ? FA_MASK_ZERO : FA_MASK_MIXED;
+}
+
 // One (query tile, key tiles kt0..kt1-1) entry for (sequence b, KV head g).
 // QS: the queries are pre-scaled by log2(e)/sqrt(128) (see FlashArgs); the
 // score MFMA chain then starts from minus the row's reference, so each
 // accumulator is the exponent of its probability with no VALU work.
-template <bool QS>
+template <bool QS, bool MASK>
 __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, int b, int g,
                                             int qt, int kt0, int kt1, int slot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -185,8 +250,10 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   float m_eff = 0.f, thr = NEG_INF;
   f32x16 negm = f32x16{};
 
-  const bool has_mask = a.mask != nullptr;
-  const float* mrow = has_mask ? a.mask + (size_t)(qi < a.T ? qi : 0) * a.kv_len : nullptr;
+  // MASK: an explicit additive mask (a kernel of its own: its loads need
+  // registers the causal and unmasked launches keep for their loop)
+  constexpr bool has_mask = MASK;
+  const float* mrow = MASK ? a.mask + (size_t)(qi < a.T ? qi : 0) * a.kv_len : nullptr;
 
   // S^T = K·Q^T for tile t into s.
   auto qk = [&](int t, f32x16 (&s)[2]) {
@@ -221,21 +288,40 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   };
 
   // The online softmax of tile t from its raw scores s, leaving P^T in pf.
-  auto softmax = [&](int t, f32x16 (&s)[2]) {
+  // mc: the tile's mask class (wave-uniform; FA_MASK_ZERO without a mask)
+  auto softmax = [&](int t, f32x16 (&s)[2], int mc) {
     // lane holds query lrow, keys 32kb + 8(i>>2) + 4*lhalf + (i&3)
     const int k0 = t * FA_BN;
-    const bool edge = (a.causal && (k0 + FA_BN - 1 > a.q_pos0 + q0)) || (k0 + FA_BN > a.kv_len) || has_mask;
+    const bool edge = (a.causal && (k0 + FA_BN - 1 > a.q_pos0 + q0)) || (k0 + FA_BN > a.kv_len) ||
+                      mc != FA_MASK_ZERO;
     if (edge) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // a mixed tile's mask values, 16 at a time: every load of a block issued
+        // before the first is used (indices clamped into the mask; the values
+        // past its end are not used), then one wait for all of them. vmcnt
+        // counts in order, so these loads complete only after the K/V tile
+        // loads issued before them anyway; the explicit wait also tells the
+        // compiler's wait-count pass that nothing is left in flight, so it
+        // puts no vmcnt(0) on the path of tiles that load no mask
+        float mv[16];
+        if (mc == FA_MASK_MIXED) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kg = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+            mv[i] = mrow[kg < a.kv_len ? kg : a.kv_len - 1];
+          }
+          wait_vmcnt<0>();
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kg = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
           float x = s[kb2][i];
-          if (has_mask && kg < a.kv_len && qi < a.T) x += mrow[kg] * (QS ? LOG2E : SQRT_DH);
-          if (kg >= a.kv_len || (a.causal && kg > qpos)) x = NEG_INF;
+          if (mc == FA_MASK_MIXED) x += mv[i] * (QS ? LOG2E : SQRT_DH);
+          if (mc == FA_MASK_NEG_INF || kg >= a.kv_len || (a.causal && kg > qpos)) x = NEG_INF;
           s[kb2][i] = x;
         }
+      }
     }
     // Lanes l and l ^ 32 hold the two halves of a query row's keys and keep the
     // same reference max. Each half tests its own maximum; only when some half
@@ -343,6 +429,19 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
 
   issue(kt0);
   if (kt0 + 1 < kt1) issue(kt0 + 1);
+  // Mask classes of this query tile's key tiles, held in a register: lane l
+  // has those of tiles cbase + 4l .. cbase + 4l + 3 (one dword of the class
+  // row), a window of 256 tiles, moved on every 256 tiles. A class is then a
+  // lane read with a uniform index, no memory access inside the loop.
+  const uint32_t* crow =
+      (MASK && a.mcls) ? reinterpret_cast<const uint32_t*>(a.mcls + (size_t)qt * a.nkp) : nullptr;
+  int cbase = kt0 & ~3;
+  uint32_t cwin = 0;
+  auto load_classes = [&]() {
+    const int wi = (cbase >> 2) + lane;
+    cwin = wi < (a.nkp >> 2) ? crow[wi] : 0u;
+  };
+  if (MASK && a.mcls) load_classes();
   // Query fragments (MFMA B operand): k-step s covers d = 16s + 8*lhalf .. +7.
   {
     const bool ok = qi < a.T;
@@ -361,19 +460,35 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   // trip t: tile t is computed (the lagging waves finish tile t-1); one extra
   // trip lets the lagging waves do the last P·V.
   f32x16 s[2];
+  int mc_prev = FA_MASK_ZERO;   // class of tile t - 1 (the lagging waves' softmax)
   for (int t = kt0; t <= kt1; ++t) {
+    int mc = FA_MASK_ZERO;       // class of tile t
+    if (MASK) {
+      mc = FA_MASK_MIXED;
+      if (a.mcls && t < kt1) {
+        if (t - cbase >= 256) {
+          // next window: waits for every load in flight, once per 256 tiles
+          cbase += 256;
+          load_classes();
+          wait_vmcnt<0>();
+        }
+        const int d = t - cbase;
+        mc = (int)(((uint32_t)__builtin_amdgcn_readlane((int)cwin, d >> 2) >> (8 * (d & 3))) & 255u);
+      }
+    }
     // tile t resident (tile t+1 may still be in flight); every wave is past
     // trip t-1, so stage (t+2)%4 — last read as tile t-2 — is free
     if (t + 1 < kt1) wait_vmcnt<FA_NI_W>(); else wait_vmcnt<0>();
     barrier_no_fence();
     if (t + 2 < kt1) issue(t + 2);
     if (!lag) {
-      if (t < kt1) { qk(t, s); softmax(t, s); pv(t); }
+      if (t < kt1) { qk(t, s); softmax(t, s, mc); pv(t); }
     } else {
       // softmax VALU work first, while the SIMD's leading wave runs its score MFMAs
-      if (t > kt0) { softmax(t - 1, s); pv(t - 1); }
+      if (t > kt0) { softmax(t - 1, s, mc_prev); pv(t - 1); }
       if (t < kt1) qk(t, s);
     }
+    mc_prev = mc;
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -409,7 +524,7 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
   }
 }
 
-template <bool QS>
+template <bool QS, bool MASK>
 __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t smem[FA_STAGES * 2 * FA_TILE];
   const int g = blockIdx.x & (N_KV - 1);
@@ -422,15 +537,37 @@ __global__ __launch_bounds__(FA_THREADS) void flash_fwd_kernel(FlashArgs a) {
       const unsigned e = a.ent[i];
       // every wave is done with the LDS ring of the previous entry
       if (i > a.bin_start[bin]) barrier_no_fence();
-      flash_entry<QS>(a, smem, b, g, e & 255, (e >> 8) & 255, (e >> 16) & 255, e >> 24);
+      flash_entry<QS, MASK>(a, smem, b, g, e & 255, (e >> 8) & 255, (e >> 16) & 255, e >> 24);
     }
     return;
   }
-  // plain launch: one query tile per workgroup, longest first when causal
-  const int qt = a.causal ? (a.n_qtiles - 1 - rest / a.B) : (rest / a.B);
+  // plain launch: one query tile per workgroup, last query tile first when
+  // causal or masked (the longest first under a causal mask, a window over a
+  // cache or a chunk's mask: the structured masks whose later rows see at
+  // least as many keys; any order is correct)
+  const int qt = (a.causal || MASK) ? (a.n_qtiles - 1 - rest / a.B) : (rest / a.B);
   int kv_end = a.kv_len;
   if (a.causal) kv_end = min(kv_end, a.q_pos0 + (qt + 1) * FA_BQ);
-  flash_entry<QS>(a, smem, b, g, qt, 0, (kv_end + FA_BN - 1) / FA_BN, FA_DIRECT);
+  int kt0 = 0, kt1 = (kv_end + FA_BN - 1) / FA_BN;
+  if (MASK && a.mcls) {
+    // key tiles from the first to the last that is not all -inf (each wave
+    // scans the query tile's classes itself; none: the rows get H = 0)
+    const int lane = threadIdx.x & 63;
+    int lo = kt1, hi = -1;
+    for (int t = lane; t < kt1; t += 64)
+      if (a.mcls[(size_t)qt * a.nkp + t] != FA_MASK_NEG_INF) { lo = min(lo, t); hi = max(hi, t); }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      lo = min(lo, __shfl_xor(lo, off));
+      hi = max(hi, __shfl_xor(hi, off));
+    }
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
+    if (hi < lo) { lo = 0; hi = -1; }
+    kt0 = lo;
+    kt1 = hi + 1;
+  }
+  flash_entry<QS, MASK>(a, smem, b, g, qt, kt0, kt1, FA_DIRECT);
 }
 
 // Combines the pieces of cut query tiles. Workgroup (r, t, b, g) takes rows
@@ -485,6 +622,13 @@ __global__ __launch_bounds__(256) void flash_merge_kernel(FlashMergeArgs a) {
 }
 
 size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal) {
+  if (!causal) {
+    // a class byte per (query tile, key tile) for an explicit mask, rows padded
+    // to a multiple of 4 bytes
+    const size_t nq = (T + FA_BQ - 1) / FA_BQ;
+    const size_t nkp = (((size_t)kv_len + FA_BN - 1) / FA_BN + 3) & ~(size_t)3;
+    return (nq * nkp + 255) & ~(size_t)255;
+  }
   FlashPlan p;
   if (!flash_plan(B, T, kv_len, q_pos0, causal, N_KV, p)) return 0;
   return (size_t)p.n_slots * B * N_KV * FA_PART * sizeof(float);
@@ -498,6 +642,18 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
   a.q = q_r; a.k = k; a.v = v; a.kv_bstride = kv_bstride; a.mask = mask; a.h = h_out;
   a.B = B; a.T = T; a.kv_len = kv_len; a.q_pos0 = q_pos0; a.causal = causal;
   a.n_qtiles = (T + FA_BQ - 1) / FA_BQ;
+  if (mask && !causal && partials) {
+    // the workspace holds the mask's tile classes (flash_partials_bytes, non-causal)
+    const int nk = (kv_len + FA_BN - 1) / FA_BN;
+    a.nkp = (nk + 3) & ~3;
+    auto* cls = reinterpret_cast<unsigned char*>(partials);
+    hipLaunchKernelGGL(flash_mask_classes_kernel, dim3((unsigned)nk, (unsigned)a.n_qtiles),
+                       dim3(256), 0, s, mask, T, kv_len, a.nkp,
+                       (int)((kv_len & 3) == 0 && (reinterpret_cast<uintptr_t>(mask) & 15) == 0), cls);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.mcls = cls;
+  }
   FlashPlan plan;
   const bool planned = partials && flash_plan(B, T, kv_len, q_pos0, causal, N_KV, plan);
   long long grid = (long long)a.n_qtiles * B * N_KV;
@@ -508,10 +664,17 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
     for (int i = 0; i < plan.n_ent; ++i) a.ent[i] = plan.ent[i];
     grid = (long long)plan.n_bins * B * N_KV;
   }
-  if (q_scaled)
-    hipLaunchKernelGGL(flash_fwd_kernel<true>, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
-  else
-    hipLaunchKernelGGL(flash_fwd_kernel<false>, dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  if (mask) {
+    if (q_scaled)
+      hipLaunchKernelGGL((flash_fwd_kernel<true, true>), dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((flash_fwd_kernel<false, true>), dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  } else {
+    if (q_scaled)
+      hipLaunchKernelGGL((flash_fwd_kernel<true, false>), dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((flash_fwd_kernel<false, false>), dim3((unsigned)grid), dim3(FA_THREADS), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !planned || plan.n_merge == 0) return e;
   FlashMergeArgs m{};

@@ -39,7 +39,10 @@ inline PrefillWs prefill_layout(int B, int T) {
   w.h = w.v + align_up(m * KV_W * 2);
   w.part = w.h + align_up(m * D_MODEL * 2);
   const size_t proj = gqa::gemm_splitk_bytes((int)m);
-  const size_t attn = gqa::flash_partials_bytes(B, T, T, 0, 1);
+  // the causal plan's partials, or an explicit mask's tile classes
+  const size_t plan = gqa::flash_partials_bytes(B, T, T, 0, 1);
+  const size_t cls = gqa::flash_partials_bytes(B, T, T, 0, 0);
+  const size_t attn = plan > cls ? plan : cls;
   w.total = w.part + align_up(proj > attn ? proj : attn);
   return w;
 }

@@ -46,9 +46,11 @@ size_t gemm_splitk_bytes(int M);
 // Prefill grouped flash attention. q_r/h_out [B][T][32][128]; k/v rows of
 // sequence b start at k + b*kv_bstride (row stride 1024 elements); query i is
 // at position q_pos0 + i; keys 0..kv_len-1. `partials` (may be null: plain
-// launch) is fp32 scratch of flash_partials_bytes(B, T, kv_len, q_pos0, causal) bytes
-// for the balanced causal launch of few query tiles. q_scaled: the queries
-// carry the factor QK_SCALE_LOG2 already (launch_qkv_rope's q_scale).
+// launch, every explicit-mask tile added element by element) is scratch of
+// flash_partials_bytes(B, T, kv_len, q_pos0, causal) bytes: fp32 piece partials
+// for the balanced causal launch of few query tiles, or (non-causal) a class
+// byte per 64x64 tile of an explicit mask (rows of tiles padded to 4 bytes). q_scaled: the queries carry the
+// factor QK_SCALE_LOG2 already (launch_qkv_rope's q_scale).
 size_t flash_partials_bytes(int B, int T, int kv_len, int q_pos0, int causal);
 hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const uint16_t* v,
                                   long long kv_bstride, const float* mask, int causal, int B,

@@ -297,10 +297,13 @@ int gqa_qkv_rope(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                  gqa_bf16* q_r, gqa_bf16* k_r, gqa_bf16* v, int q_scaled, void* stream);
 
 /*
- * Workspace bytes gqa_attention uses to balance a causal launch with few query
- * tiles (the last query tile attends to every key tile, so with fewer than two
- * 64-row tiles per CU the longest workgroup would set the time). 0 when the
- * launch needs none (non-causal, or enough query tiles).
+ * Workspace bytes gqa_attention uses: for a causal launch with few query tiles,
+ * the balanced plan's partials (the last query tile attends to every key tile,
+ * so with fewer than two 64-row tiles per CU the longest workgroup would set
+ * the time; 0 with enough query tiles); for a non-causal launch, one byte per
+ * 64x64 tile of the mask (its class: all 0, all -inf or mixed; each row of
+ * tiles padded to a multiple of 4 bytes, the total to a multiple of 256), so
+ * that an explicit mask costs about what the same mask given as a flag costs.
  */
 size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal);
 
@@ -310,9 +313,11 @@ size_t gqa_attention_workspace_bytes(int B, int T, int kv_len, int causal);
  *   q_r [B][T][32][128], k_r and v [B][kv_len][8][128]   bf16
  *   mask / causal as for gqa_block_forward (kv_len must equal T)
  *   h_out [B][T][32][128]   bf16 out
- *   workspace   NULL (plain launch), or >= gqa_attention_workspace_bytes(B, T,
- *               kv_len, causal) bytes of device memory (balanced launch; the
- *               result is the same up to fp32 summation order)
+ *   workspace   NULL (plain launch; an explicit mask is then added tile by
+ *               tile everywhere), or >= gqa_attention_workspace_bytes(B, T,
+ *               kv_len, causal) bytes of device memory (balanced causal launch,
+ *               the same result up to fp32 summation order; or the mask's tile
+ *               classes, the same result bit for bit)
  *   q_scaled    0: q_r is Q_r; 1: q_r is Q_r times log2(e)/sqrt(128), as
  *               gqa_qkv_rope writes it with q_scaled = 1 (the kernel the block
  *               and chunk entries run: it spends no instruction on the scale)

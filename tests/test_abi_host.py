@@ -80,14 +80,18 @@ def test_rope_table_from_frequencies():
 def test_workspace_sizes():
     M = 8 * 4096   # enough query tiles: no balanced-attention partials, no split reduction
     want = sum(((M * f * 2 + 255) // 256) * 256 for f in (4096, 1024, 1024, 4096))
-    assert gqa.prefill_workspace_bytes(8, 4096) == want
+    # plus a class byte per 64x64 tile of an explicit mask (64 x 64 tiles)
+    assert gqa.prefill_workspace_bytes(8, 4096) == want + 64 * 64
     assert gqa.prefill_workspace_bytes(0, 5) == 0
     # few query tiles, causal: fp32 partials of the cut query tiles; the prefill
     # workspace covers them; plain launches need none
     att = gqa.attention_workspace_bytes(1, 2048, 2048, True)
     assert att > 0 and att % (8 * (4 * 64 * 128 + 2 * 4 * 64) * 4) == 0
     assert gqa.prefill_workspace_bytes(1, 2048) >= 2048 * 10240 * 2 + att
-    assert gqa.attention_workspace_bytes(1, 2048, 2048, False) == 0
+    # non-causal: the explicit mask's tile classes, one byte per 64x64 tile
+    assert gqa.attention_workspace_bytes(1, 2048, 2048, False) == 32 * 32
+    assert gqa.attention_workspace_bytes(1, 100, 100, False) == 256   # 2 x 2 tiles, rounded
+    assert gqa.attention_workspace_bytes(1, 1100, 1100, False) == 512  # 18 rows of 18 (+2 pad) tiles
     assert gqa.attention_workspace_bytes(8, 4096, 4096, True) == 0
     assert gqa.attention_workspace_bytes(1, 128, 128, True) == 0
     # M <= 64 tokens: the projections' split-reduction partials (4 x M x 6144 fp32)

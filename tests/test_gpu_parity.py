@@ -237,6 +237,66 @@ def test_attention_window_mask_rows_start_late():
                                mask.astype(np.float64))
     assert_close(got, want, rel=STAGE_REL, what="H (window mask)")
 
+@pytest.mark.parametrize("B,T,W", [(2, 700, 160), (1, 333, 100)])
+def test_attention_structured_mask_by_tile_classes(B, T, W):
+    # An explicit mask is classified per 64x64 tile when the launch has a
+    # workspace (all 0: the add is skipped; all -inf: the tile is skipped or
+    # its keys removed; else added element by element). A sliding window of W
+    # keys has all three classes, a ragged last tile in both directions, and
+    # key tiles before the window that the walk skips; query tile 1 is masked
+    # whole (its rows get H = 0). Without a workspace every tile takes the
+    # element-wise add: both launches must agree bit for bit, and match the
+    # oracle.
+    print(f"[case] attention window mask classes B={B} T={T} W={W}", flush=True)
+    q, k, v = _qkv_direct(416 + T, B, T)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    mask = np.where((j <= i) & (j > i - W), 0.0, -np.inf).astype(np.float32)
+    mask[64:128] = -np.inf
+    qd, kd, vd, md = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v), to_dev_f32(mask)
+    assert gqa.attention_workspace_bytes(B, T, T, False) > 0
+    h_cls = gqa.attention(qd, kd, vd, causal=False, mask=md)
+    h_elt = gqa.attention(qd, kd, vd, causal=False, mask=md, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_cls, h_elt), "tile classes must not change a bit of H"
+    got = bf16_to_np_f64(h_cls)
+    assert np.all(got[:, 64:128] == 0.0), "a query tile masked whole must give H = 0"
+    live = np.r_[0:64, 128:T]
+    ok_mask = mask.astype(np.float64)
+    ok_mask[64:128, 0] = 0.0                            # any defined row; not compared
+    want = O.grouped_attention(O.bf16_to_f64(q), O.bf16_to_f64(k), O.bf16_to_f64(v), ok_mask)
+    assert_close(got[:, live], want[:, live], rel=STAGE_REL, what="H (window mask, classes)")
+
+
+def test_attention_mask_classes_past_256_key_tiles():
+    # The attention kernel holds a query tile's mask classes 256 key tiles at a
+    # time; at T = 16484 (258 key tiles, the last ragged) the last query tiles
+    # move to a second window. The mask: causal, key tiles 100 and 101 all -inf
+    # (inside every later query tile's walk), a mixed tile in the second window
+    # (keys 16400..16419 shifted by +0.75) and one in the first (-1.5 on
+    # query tile 125, key tile 2). Bitwise against the element-wise launch
+    # (no workspace); sampled rows against the oracle.
+    B, T = 1, 16484
+    print(f"[case] attention mask classes over two windows B={B} T={T}", flush=True)
+    q, k, v = _qkv_direct(418, B, T)
+    m = torch.triu(torch.full((T, T), float("-inf"), device=dev()), diagonal=1)
+    m[:, 6400:6528] = float("-inf")
+    m[:, 16400:16420] += 0.75
+    m[8000:8064, 128:192] = -1.5
+    qd, kd, vd = to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v)
+    h_cls = gqa.attention(qd, kd, vd, causal=False, mask=m)
+    h_elt = gqa.attention(qd, kd, vd, causal=False, mask=m, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_cls, h_elt), "tile classes must not change a bit of H"
+    rows = np.array([0, 6399, 6400, 8000, 8063, 16383, 16384, 16419, T - 1])
+    mrows = m[torch.from_numpy(rows).to(dev())].cpu().numpy().astype(np.float64)
+    del m
+    torch.cuda.empty_cache()
+    want = O.grouped_attention(O.bf16_to_f64(q[:, rows]), O.bf16_to_f64(k), O.bf16_to_f64(v), mrows)
+    got = bf16_to_np_f64(h_cls[:, torch.from_numpy(rows).to(dev())])
+    assert_close(got, want, rel=STAGE_REL, what="H (two class windows, sampled rows)")
+
+
 @pytest.mark.parametrize("q_scaled", [False, True])
 def test_attention_fully_masked_rows_give_zero(q_scaled):
     # A row whose every key the caller's mask removes has no defined softmax
