@@ -46,11 +46,11 @@ PARAMS_PER_BLOCK = 41_943_040  # W_Q + W_K + W_V + W_O
 PROFILED_TRAFFIC = {
     ("prefill_B1_T2048", "qkv_rope"): {"kernel": "gemm_nt_kernel<256, 192, 2, 4, 2, 0, 64>",
                                        "bytes": 197.3e6},
-    ("prefill_B1_T2048", "attention"): {"kernel": "flash_fwd_kernel<true> + flash_merge_kernel",
+    ("prefill_B1_T2048", "attention"): {"kernel": "flash_fwd_kernel<true, false> + flash_merge_kernel",
                                         "bytes": 102.1e6},
     ("prefill_B1_T2048", "out_proj"): {"kernel": "gemm_nt_kernel<128, 256, 2, 4, 2, 1, 64>",
                                        "bytes": 167.9e6},
-    ("prefill_B1_T131072", "attention"): {"kernel": "flash_fwd_kernel<true> (plain causal launch)",
+    ("prefill_B1_T131072", "attention"): {"kernel": "flash_fwd_kernel<true, false> (plain causal launch)",
                                           "bytes": 19.595e9},
 }
 
@@ -222,8 +222,8 @@ class Bench:
             "qkv_rope": ("gemm_nt_kernel (fused QKV GEMM + rotation epilogue)",
                          lambda: gqa.qkv_rope(x, w[0], w[1], w[2], rope, q_r=q_r, k_r=k_r, v=v,
                                               q_scaled=True)),
-            "attention": ("flash_fwd_kernel<true> + flash_merge_kernel (balanced causal launch)"
-                          if aws_n else "flash_fwd_kernel<true> (pre-scaled queries)",
+            "attention": ("flash_fwd_kernel<true, false> + flash_merge_kernel (balanced causal launch)"
+                          if aws_n else "flash_fwd_kernel<true, false> (pre-scaled queries)",
                           lambda: gqa.attention(q_r, k_r, v, causal=True, h_out=hbuf,
                                                 workspace=aws if aws_n else None,
                                                 q_scaled=True)),
