@@ -96,7 +96,10 @@ int gqa_rope_table(const int32_t* positions, int n, double theta, float* table);
  */
 int gqa_rope_table_freqs(const int32_t* positions, int n, const double* omega, float* table);
 
-/* Workspace bytes gqa_block_forward needs for B sequences of T positions. */
+/* Workspace bytes gqa_block_forward needs for B sequences of T positions
+ * (the bf16 Q_r, K_r, V and H of the step, plus the larger of the projections'
+ * split-reduction partials and the attention stage's own workspace: the
+ * causal plan's partials, or an explicit mask's tile classes). */
 size_t gqa_prefill_workspace_bytes(int B, int T);
 
 /*
@@ -120,7 +123,10 @@ size_t gqa_prefill_workspace_bytes(int B, int T);
  *   h_out  [B][T][32][128] bf16 merged head outputs H, or NULL
  *   workspace                   >= gqa_prefill_workspace_bytes(B, T) bytes
  * Kernels: fused QKV projection + rotation, grouped flash attention, output
- * projection. A row whose every key is masked by `mask` yields H = 0.
+ * projection. A row whose every key is masked by `mask` yields H = 0. An
+ * explicit mask is first classified per 64x64 tile (all 0 / all -inf / mixed),
+ * so key tiles it removes whole are never loaded; the result is the one of
+ * adding it element by element, bit for bit.
  */
 int gqa_block_forward(const gqa_bf16* x, const gqa_bf16* w_q, const gqa_bf16* w_k,
                       const gqa_bf16* w_v, const gqa_bf16* w_o, const float* rope,
