@@ -268,6 +268,40 @@ def test_attention_structured_mask_by_tile_classes(B, T, W):
     assert_close(got[:, live], want[:, live], rel=STAGE_REL, what="H (window mask, classes)")
 
 
+@pytest.mark.parametrize("q_scaled", [False, True])
+def test_attention_mask_random_tile_classes(q_scaled):
+    # Each 64x64 tile of the mask drawn at random as all 0, all -inf or N(0, 1)
+    # values (T = 1000: the last tiles ragged both ways), so every class sits
+    # next to every other and some query tiles see only a few key tiles, not
+    # the first or last ones. Bitwise against the element-wise launch; rows
+    # with a visible key against the oracle, rows with none exactly zero.
+    B, T = 2, 1000
+    print(f"[case] attention random tile classes B={B} T={T} q_scaled={q_scaled}", flush=True)
+    q, k, v = _qkv_direct(419, B, T)
+    rng = np.random.Generator(np.random.PCG64(420))
+    nt = (T + 63) // 64
+    cls = rng.integers(0, 3, (nt, nt)).repeat(64, 0).repeat(64, 1)[:T, :T]
+    mask = np.where(cls == 0, 0.0, np.where(cls == 1, -np.inf,
+                                            rng.standard_normal((T, T)))).astype(np.float32)
+    c = np.log2(np.e) / np.sqrt(128.0)
+    qd = gi.f32_to_bf16_bits((O.bf16_to_f64(q) * c).astype(np.float32)) if q_scaled else q
+    args = (to_dev_bf16(qd), to_dev_bf16(k), to_dev_bf16(v))
+    md = to_dev_f32(mask)
+    h_cls = gqa.attention(*args, causal=False, mask=md, q_scaled=q_scaled)
+    h_elt = gqa.attention(*args, causal=False, mask=md, q_scaled=q_scaled, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_cls, h_elt), "tile classes must not change a bit of H"
+    got = bf16_to_np_f64(h_cls)
+    dead = np.all(mask == -np.inf, axis=1)
+    assert np.all(got[:, dead] == 0.0)
+    live = np.nonzero(~dead)[0]
+    assert len(live) > T // 2
+    qo = O.bf16_to_f64(qd) / c if q_scaled else O.bf16_to_f64(q)
+    want = O.grouped_attention(qo[:, live], O.bf16_to_f64(k), O.bf16_to_f64(v),
+                               mask[live].astype(np.float64))
+    assert_close(got[:, live], want, rel=STAGE_REL, what="H (random tile classes)")
+
+
 def test_attention_mask_classes_past_256_key_tiles():
     # The attention kernel holds a query tile's mask classes 256 key tiles at a
     # time; at T = 16484 (258 key tiles, the last ragged) the last query tiles
