@@ -302,6 +302,28 @@ def test_attention_mask_random_tile_classes(q_scaled):
     assert_close(got[:, live], want, rel=STAGE_REL, what="H (random tile classes)")
 
 
+@pytest.mark.parametrize("T", [1, 63, 65])
+def test_attention_mask_classes_small_shapes(T):
+    # one position (a single ragged tile), one tile short of full, one key
+    # past a tile: random mask with -inf entries, key 0 kept for every row
+    B = 2
+    print(f"[case] attention mask classes B={B} T={T}", flush=True)
+    q, k, v = _qkv_direct(430 + T, B, T)
+    rng = np.random.Generator(np.random.PCG64(431 + T))
+    mask = rng.standard_normal((T, T)).astype(np.float32)
+    mask[rng.random((T, T)) < 0.4] = -np.inf
+    mask[:, 0] = 0.0
+    args = (to_dev_bf16(q), to_dev_bf16(k), to_dev_bf16(v))
+    md = to_dev_f32(mask)
+    h_cls = gqa.attention(*args, causal=False, mask=md)
+    h_elt = gqa.attention(*args, causal=False, mask=md, balanced=False)
+    torch.cuda.synchronize()
+    assert torch.equal(h_cls, h_elt)
+    want = O.grouped_attention(O.bf16_to_f64(q), O.bf16_to_f64(k), O.bf16_to_f64(v),
+                               mask.astype(np.float64))
+    assert_close(bf16_to_np_f64(h_cls), want, rel=STAGE_REL, what=f"H (mask classes, T={T})")
+
+
 def test_attention_mask_classes_past_256_key_tiles():
     # The attention kernel holds a query tile's mask classes 256 key tiles at a
     # time; at T = 16484 (258 key tiles, the last ragged) the last query tiles
