@@ -542,6 +542,60 @@ class Bench:
             print(json.dumps({"vendor_gemm": name, "M": M, "median_ms": round(ms, 5),
                               "TFLOP/s": round(F / (ms * 1e-3) / 1e12, 1)}), flush=True)
 
+    def mask_timing(self, reps=8):
+        """Context only: the attention stage (pre-scaled queries, B = 1) with the
+        causal flag, with the same causal mask passed explicitly (through its
+        64x64 tile classes, and added element by element without a workspace),
+        with a sliding window of 1024 keys and with no mask; legs alternated in
+        one process, each timed over back-to-back calls (so the host's launch
+        work overlaps the GPU's, as inside a block step), median of `reps`."""
+        torch, gqa = self.torch, self.gqa
+        g = torch.Generator(device=self.dev)
+        g.manual_seed(6)
+        NEG = float("-inf")
+        for T in (2048, 8192):
+            def rnd_bf16(shape, std):
+                return (torch.randn(shape, device=self.dev, generator=g) * std).to(torch.bfloat16)
+            q = rnd_bf16((1, T, 32, 128), 0.16)
+            k = rnd_bf16((1, T, 8, 128), 1.28)
+            v = rnd_bf16((1, T, 8, 128), 1.28)
+            h = torch.empty_like(q)
+            i = torch.arange(T, device=self.dev)[:, None]
+            j = torch.arange(T, device=self.dev)[None, :]
+            causal = torch.where(j <= i, 0.0, NEG).contiguous()
+            window = torch.where((j <= i) & (j > i - 1024), 0.0, NEG).contiguous()
+            att = lambda **kw: gqa.attention(q, k, v, h_out=h, q_scaled=True, **kw)
+            legs = [("causal flag", lambda: att(causal=True)),
+                    ("causal flag, plain launch", lambda: att(causal=True, balanced=False)),
+                    ("explicit causal mask (tile classes)", lambda: att(causal=False, mask=causal)),
+                    ("explicit causal mask, element-wise", lambda: att(causal=False, mask=causal,
+                                                                       balanced=False)),
+                    ("window of 1024 keys (tile classes)", lambda: att(causal=False, mask=window)),
+                    ("no mask", lambda: att(causal=False))]
+            calls = 8 if T <= 2048 else 2
+            times = {name: [] for name, _ in legs}
+            for it in range(reps + 1):
+                for name, fn in legs:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    for _ in range(calls):
+                        fn()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    if it:
+                        times[name].append(e0.elapsed_time(e1) / calls)
+            att(causal=False, mask=causal)
+            h_cls = h.clone()
+            att(causal=False, mask=causal, balanced=False)
+            same = bool(torch.equal(h_cls, h))
+            for name, t in times.items():
+                t.sort()
+                print(json.dumps({"mask_timing": name, "B": 1, "T": T,
+                                  "median_ms": round(t[len(t) // 2], 5),
+                                  "classes_bitwise_equal_element_wise": same}), flush=True)
+            del q, k, v, h, causal, window, h_cls
+
     def calibrate_copy(self, mib):
         torch = self.torch
         n = mib << 20
@@ -569,6 +623,9 @@ def main():
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="only time the projection stages at M = 32768 beside the vendor "
                          "BLAS on the same operands (context, not a bench line)")
+    ap.add_argument("--mask-timing", action="store_true",
+                    help="only time the attention stage with the causal flag against the "
+                         "same mask passed explicitly, a sliding window and no mask (context)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
@@ -581,6 +638,9 @@ def main():
         return
     if args.vendor_gemm:
         b.vendor_gemm()
+        return
+    if args.mask_timing:
+        b.mask_timing()
         return
     extras = {"chunk": b.chunk, "prenorm": b.prenorm, "mlp": b.mlp}
     if args.only:
