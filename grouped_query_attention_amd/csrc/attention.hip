@@ -109,6 +109,9 @@ struct FlashArgs {
   // multiple of 4) bytes; null: every tile mixed
   const unsigned char* mcls;
   int nkp;
+  // the mask rows are 16-byte aligned (aligned base, kv_len a multiple of 4):
+  // a mixed tile's values are read four keys per load
+  int mask_vec;
 };
 
 struct FlashMergeArgs {
@@ -306,10 +309,22 @@ __device__ __forceinline__ void flash_entry(const FlashArgs& a, uint16_t* smem, 
         // puts no vmcnt(0) on the path of tiles that load no mask
         float mv[16];
         if (mc == FA_MASK_MIXED) {
+          if (a.mask_vec) {
+            // the lane's keys come in runs of four (i & 3), 16-byte aligned; a
+            // run past the last key is read from the mask's last four (unused)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kg = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
-            mv[i] = mrow[kg < a.kv_len ? kg : a.kv_len - 1];
+            for (int c = 0; c < 4; ++c) {
+              const int kg = k0 + kb2 * 32 + 8 * c + 4 * lhalf;
+              const f32x4 m4 = *reinterpret_cast<const f32x4*>(mrow + (kg < a.kv_len ? kg : a.kv_len - 4));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) mv[4 * c + e] = m4[e];
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int kg = k0 + kb2 * 32 + 8 * (i >> 2) + 4 * lhalf + (i & 3);
+              mv[i] = mrow[kg < a.kv_len ? kg : a.kv_len - 1];
+            }
           }
           wait_vmcnt<0>();
         }
@@ -642,6 +657,7 @@ hipError_t launch_flash_attention(const uint16_t* q_r, const uint16_t* k, const 
   a.q = q_r; a.k = k; a.v = v; a.kv_bstride = kv_bstride; a.mask = mask; a.h = h_out;
   a.B = B; a.T = T; a.kv_len = kv_len; a.q_pos0 = q_pos0; a.causal = causal;
   a.n_qtiles = (T + FA_BQ - 1) / FA_BQ;
+  a.mask_vec = mask && (kv_len & 3) == 0 && (reinterpret_cast<uintptr_t>(mask) & 15) == 0;
   if (mask && !causal && partials) {
     // the workspace holds the mask's tile classes (flash_partials_bytes, non-causal)
     const int nk = (kv_len + FA_BN - 1) / FA_BN;
