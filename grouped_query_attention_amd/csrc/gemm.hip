@@ -634,10 +634,13 @@ static hipError_t launch_gemm_splitk(GemmArgs a, float* part, hipStream_t s) {
 }
 
 // Split reduction for few tokens (with a workspace): M <= 64 takes one 64-token
-// tile and 4 slices of K (weight streams, non-temporal); 64 < M <= 256 takes
-// 128-token tiles and 8 slices up to M = 128, 4 above, so that a launch still
-// has 256-768 workgroups (unsplit 128x128 tiles give 48 workgroups for the QKV
-// product at M = 128) while the partials stay within 1024 rows of 6144 floats.
+// tile and 4 slices of K (weight streams, non-temporal); 64 < M <= 128 takes
+// 128-token x 64-feature tiles and 4 slices (384 workgroups for the QKV
+// product, 256 for W_O; the block step at M = 128 12 % faster than 128x128
+// tiles in 8 slices, whose partials were twice as many); 128 < M <= 256 takes
+// 128x128 tiles and 4 slices (the 64-feature tiles are 5-7 % slower there).
+// Unsplit 128x128 tiles would give 48 workgroups for the QKV product at
+// M = 128; the partials stay within 1024 rows of 6144 floats.
 constexpr int SPLITK_MAX_M = 64;
 constexpr int SPLITK = 4;
 constexpr int SPLITK_MID_M = 256;
@@ -645,7 +648,7 @@ constexpr int GEMM_CUS = 256;   // CUs a launch is sized for (MI355X)
 
 // K slices of the split reduction for M tokens (0: not split)
 inline int splitk_slices(int M) {
-  return M <= SPLITK_MAX_M ? SPLITK : M <= 128 ? 8 : M <= SPLITK_MID_M ? 4 : 0;
+  return M <= SPLITK_MID_M ? SPLITK : 0;
 }
 
 size_t gemm_splitk_bytes(int M) {
@@ -660,7 +663,7 @@ size_t gemm_splitk_bytes(int M) {
 static hipError_t launch_fp32_out(GemmArgs a, float* splitk, hipStream_t s) {
   const int M = a.M;
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 64, 2, 2, 4, SPLITK>(a, splitk, s);
-  if (M <= 128 && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 8>(a, splitk, s);
+  if (M <= 128 && splitk) return launch_gemm_splitk<128, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= SPLITK_MID_M && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 4>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 2, 1, 8, EPI_OUT_F32>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_OUT_F32>(a, s);
@@ -681,7 +684,7 @@ hipError_t launch_qkv_rope(const uint16_t* x, const uint16_t* wq, const uint16_t
   // Few tokens (decode): split K with a workspace, else thin weight strips and a
   // deep load ring; otherwise the largest tile that still fills the chip.
   if (M <= SPLITK_MAX_M && splitk) return launch_gemm_splitk<64, 128, 2, 2, 4, SPLITK>(a, splitk, s);
-  if (M <= 128 && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 8>(a, splitk, s);
+  if (M <= 128 && splitk) return launch_gemm_splitk<128, 64, 2, 2, 4, SPLITK>(a, splitk, s);
   if (M <= SPLITK_MID_M && splitk) return launch_gemm_splitk<128, 128, 2, 2, 3, 4>(a, splitk, s);
   if (M <= 64) return launch_gemm<64, 32, 1, 2, 8, EPI_QKV_ROPE>(a, s);
   if (M <= 1024) return launch_gemm<128, 128, 2, 2, 2, EPI_QKV_ROPE>(a, s);

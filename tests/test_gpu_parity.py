@@ -386,8 +386,8 @@ def test_attention_fully_masked_rows_give_zero(q_scaled):
 # --- whole block ---------------------------------------------------------------------
 
 # (2, 30): 60 tokens take the projections' split-reduction path with 64-token
-# tiles (M <= 64); (1, 128) and (2, 77): 128-token tiles in 8 slices (M <= 128);
-# (2, 100): in 4 slices (M <= 256); (3, 129): unsplit
+# tiles (M <= 64); (1, 128) and (2, 77): 128-token x 64-feature tiles in 4
+# slices (M <= 128); (2, 100): 128x128 tiles in 4 slices (M <= 256); (3, 129): unsplit
 @pytest.mark.parametrize("B,T,seed", [(1, 128, 1), (2, 77, 21), (3, 129, 22), (1, 1, 23),
                                       (2, 30, 24), (2, 100, 25)])
 def test_block_forward_small(B, T, seed):
@@ -560,7 +560,8 @@ def _decode(inp, start_pos):
 
 # (6, 700, 672) and (3, 1400, 1360): 16-key chunks, several one-tile items per
 # persistent workgroup (each item's queries must survive the ring's lookahead)
-# (100, 300, 299) and (200, 64, 63): projections split in 8 and 4 slices
+# (100, 300, 299) and (200, 64, 63): projections split in 4 slices (128x64 and
+# 128x128 tiles)
 @pytest.mark.parametrize("B,S_max,start_pos", [(3, 700, 650), (2, 40, 0), (1, 1024, 1023),
                                                (2, 600, 511), (6, 700, 672), (3, 1400, 1360),
                                                (100, 300, 299), (200, 64, 63)])
